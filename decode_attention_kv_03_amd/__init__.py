@@ -1,0 +1,27 @@
+"""kvattn: single-token decode attention over a KV cache for MI355X (gfx950).
+
+Two operations, both hand-written HIP kernels behind a C ABI
+(``include/kvattn.h``, built into ``libkvattn.so`` next to this file):
+
+* ``gqa_decode`` -- grouped-query decode: ``h`` query heads share ``g``
+  cached K/V heads (MHA when ``g = h``, MQA when ``g = 1``), over a
+  contiguous or block-table-paged cache with per-sequence lengths.
+* ``mla_decode`` -- absorbed multi-head latent attention decode: every head
+  scores an absorbed 576-wide query against cached ``[latent 512 | RoPE 64]``
+  rows and accumulates its output in the 512-wide latent space.
+
+The Python layer only marshals arguments (device pointers, sizes, the
+current HIP stream); every arithmetic step runs in the library's kernels.
+Importing this package does not load the library; the first call does, and
+raises if the library is missing or no GPU is present.
+"""
+
+from .kvattn import (  # noqa: F401
+    KvattnError,
+    gqa_decode,
+    gqa_workspace_bytes,
+    library_path,
+    load_library,
+    mla_decode,
+    mla_workspace_bytes,
+)

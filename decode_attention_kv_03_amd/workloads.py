@@ -1,0 +1,207 @@
+"""Seeded synthetic inputs for decode attention over a KV cache.
+
+This module holds random draws and input layout only (shapes, dtypes, the
+per-sequence lengths and the block table of a paged cache); it does none of
+the attention arithmetic.  The GPU tests, the bench and the CPU reference
+checks all take their inputs from here, so both sides of a parity check see
+the same bytes.
+
+The named workloads are the shapes the pages discuss, made concrete:
+Llama-3-8B-shaped and Llama-3-70B-shaped decode layers (the GQA dial at its
+MHA, GQA-8 and MQA settings, "MQA, GQA, and MLA" sections 2-4), a paged cache
+with ragged lengths ("Compressing the KV Cache ...", KV-Cache Management
+Guardrails), and a DeepSeek-V2-shaped absorbed-MLA layer (128 heads, latent
+512 + RoPE 64, "MQA, GQA, and MLA" section 5).  Values are iid N(0,1) drawn
+in float32 and rounded to the storage dtype (round to nearest even).
+"""
+
+from dataclasses import dataclass, replace
+import math
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class GqaWorkload:
+    name: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    seq_len: int  # contiguous: every sequence's length and the cache capacity; paged: maximum length
+    dtype: str  # "f32" or "bf16"
+    seed: int
+    scale: float
+    block_size: int = 0  # 0: contiguous cache [B, g, S, d]; else pool [num_blocks, g, block_size, d]
+
+    @property
+    def paged(self):
+        return self.block_size > 0
+
+
+@dataclass(frozen=True)
+class MlaWorkload:
+    name: str
+    batch: int
+    num_heads: int
+    seq_len: int
+    seed: int
+    scale: float
+    d_latent: int = 512
+    d_rope: int = 64
+    dtype: str = "bf16"
+    block_size: int = 0  # 0: contiguous [B, S, d_latent + d_rope]; else pool [num_blocks, block_size, 576]
+
+    @property
+    def paged(self):
+        return self.block_size > 0
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        GqaWorkload("gqa_h8_g2_d128_s512_b1_f32", 1, 8, 2, 128, 512, "f32", 1, 1 / math.sqrt(128)),
+        GqaWorkload("llama3_8b_gqa_h32_g8_b16_s8192", 16, 32, 8, 128, 8192, "bf16", 2, 1 / math.sqrt(128)),
+        GqaWorkload("llama3_70b_mha_h64_g64_b8_s8192", 8, 64, 64, 128, 8192, "bf16", 31, 1 / math.sqrt(128)),
+        GqaWorkload("llama3_70b_gqa_h64_g8_b64_s8192", 64, 64, 8, 128, 8192, "bf16", 32, 1 / math.sqrt(128)),
+        GqaWorkload("llama3_70b_mqa_h64_g1_b64_s8192", 64, 64, 1, 128, 8192, "bf16", 33, 1 / math.sqrt(128)),
+        GqaWorkload("paged_gqa_h64_g8_b128_bs16_len1_32768", 128, 64, 8, 128, 32768, "bf16", 4, 1 / math.sqrt(128), 16),
+        MlaWorkload("deepseek_v2_mla_h128_b32_s8192", 32, 128, 8192, 5, 1 / math.sqrt(192)),
+    ]
+}
+
+
+def torch_dtype(name):
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def _randn(shape, gen, device, dtype, chunks=1):
+    """iid N(0,1) drawn in float32 then rounded to ``dtype``; drawn in ``chunks`` slabs along dim 0."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    n0 = shape[0]
+    step = max(1, (n0 + chunks - 1) // chunks)
+    for a in range(0, n0, step):
+        b = min(n0, a + step)
+        out[a:b] = torch.randn((b - a, *shape[1:]), generator=gen, device=device, dtype=torch.float32).to(dtype)
+    return out
+
+
+def ragged_lengths_and_table(batch, max_len, block_size, seed):
+    """Paged-cache structure: lengths uniform on {1..max_len}, then a random permutation of physical blocks.
+
+    Logical blocks are enumerated sequence by sequence; sequence ``b``'s k-th
+    block is ``perm[offset_b + k]``; unused table entries are -1.  Returns
+    (lens int32 [B], table int32 [B, ceil(max_len/block_size)], num_blocks).
+    """
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, max_len + 1, size=batch)
+    nblk = (lens + block_size - 1) // block_size
+    num_blocks = int(nblk.sum())
+    perm = rng.permutation(num_blocks)
+    max_blocks = (max_len + block_size - 1) // block_size
+    table = np.full((batch, max_blocks), -1, dtype=np.int64)
+    off = 0
+    for b in range(batch):
+        table[b, : nblk[b]] = perm[off : off + nblk[b]]
+        off += int(nblk[b])
+    return lens.astype(np.int32), table.astype(np.int32), num_blocks
+
+
+def make_gqa_inputs(w, device="cpu", lens=None, poison_tail=False):
+    """Inputs for one GQA/MHA/MQA decode step.
+
+    Returns a dict with q [B,h,d], k, v (contiguous [B,g,S,d] or pool
+    [N,g,bs,d]), seq_lens int32 [B], block_table int32 [B, max_blocks] or
+    None, all on ``device``.  ``lens`` overrides the per-sequence lengths of a
+    contiguous cache (default: every sequence is full).  With
+    ``poison_tail`` every cache slot past a sequence's length holds NaN.
+    """
+    gen = torch.Generator(device=device).manual_seed(w.seed)
+    dt = torch_dtype(w.dtype)
+    B, h, g, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    q = _randn((B, h, d), gen, device, dt)
+    if w.paged:
+        lens_np, table, N = ragged_lengths_and_table(B, w.seq_len, w.block_size, w.seed)
+        k = _randn((N, g, w.block_size, d), gen, device, dt, chunks=16)
+        v = _randn((N, g, w.block_size, d), gen, device, dt, chunks=16)
+        bt = torch.from_numpy(table).to(device)
+    else:
+        lens_np = np.full(B, w.seq_len, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
+        k = _randn((B, g, w.seq_len, d), gen, device, dt, chunks=B)
+        v = _randn((B, g, w.seq_len, d), gen, device, dt, chunks=B)
+        bt = None
+    if poison_tail:
+        _poison(k, v, lens_np, bt, w.block_size)
+    return {
+        "q": q,
+        "k": k,
+        "v": v,
+        "seq_lens": torch.from_numpy(lens_np.astype(np.int32)).to(device),
+        "block_table": bt,
+        "workload": w,
+    }
+
+
+def make_mla_inputs(w, device="cpu", lens=None, poison_tail=False):
+    """Inputs for one absorbed-MLA decode step: q [B,h,576], cache [B,S,576] or pool [N,bs,576]."""
+    gen = torch.Generator(device=device).manual_seed(w.seed)
+    dt = torch_dtype(w.dtype)
+    B, h, width = w.batch, w.num_heads, w.d_latent + w.d_rope
+    q = _randn((B, h, width), gen, device, dt)
+    if w.paged:
+        lens_np, table, N = ragged_lengths_and_table(B, w.seq_len, w.block_size, w.seed)
+        cache = _randn((N, w.block_size, width), gen, device, dt, chunks=16)
+        bt = torch.from_numpy(table).to(device)
+    else:
+        lens_np = np.full(B, w.seq_len, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
+        cache = _randn((B, w.seq_len, width), gen, device, dt, chunks=B)
+        bt = None
+    if poison_tail:
+        _poison(cache, None, lens_np, bt, w.block_size)
+    return {
+        "q": q,
+        "cache": cache,
+        "seq_lens": torch.from_numpy(lens_np.astype(np.int32)).to(device),
+        "block_table": bt,
+        "workload": w,
+    }
+
+
+def _poison(k, v, lens_np, bt, block_size):
+    """Fill every cache slot past each sequence's length with NaN (catches reads past the end)."""
+    nan = float("nan")
+    for t in (k, v):
+        if t is None:
+            continue
+        if bt is None:
+            for b, n in enumerate(lens_np):
+                if t.dim() == 4:
+                    t[b, :, int(n):] = nan
+                else:
+                    t[b, int(n):] = nan
+        else:
+            table = bt.cpu().numpy()
+            for b, n in enumerate(lens_np):
+                n = int(n)
+                if n % block_size:
+                    blk = int(table[b, n // block_size])
+                    if t.dim() == 4:
+                        t[blk, :, n % block_size:] = nan
+                    else:
+                        t[blk, n % block_size:] = nan
+
+
+def host_view(t):
+    """Host copy in the form the CPU reference takes: float64 for f32, uint16 bit patterns for bf16."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype in (torch.int32, torch.int64):
+        return t.numpy()
+    return t.to(torch.float64).numpy()
+
+
+def shrink(w, **kw):
+    """Same workload with some fields replaced (smaller batch or length for CPU-sized checks)."""
+    return replace(w, **kw)
