@@ -1,0 +1,251 @@
+"""Decode-attention benchmark: one decode step of one layer per timed step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full library call (split-K kernel plus, when the call splits,
+the log-sum-exp merge) over the workload's synthetic inputs, already
+resident in HBM.  The default workload is the Llama-3-8B-shaped GQA layer
+(h=32, g=8, d=128, bf16, batch 16, every sequence 8192 tokens).  Prints one
+JSON line: throughput in sequence-steps per second per layer, the roofline
+of the decode call (algorithmic HBM bytes / measured call time against the
+8 TB/s HBM3E peak; for MLA also its matrix-core rate against 2.5 PFLOP/s),
+and the fp64 CPU reference timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn achieved HBM GB/s (% peak) + MFMA util (MLA); seq-steps/s per layer"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+DEFAULT_WORKLOAD = "llama3_8b_gqa_h32_g8_b16_s8192"
+ROTATE_BYTES = 1 << 30  # rotate input copies until at least this many distinct bytes are cycled
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--split-tokens", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def algorithmic(w, lens):
+    """Algorithmic HBM bytes and FLOPs of one decode call (per launch).
+
+    Bytes: every valid cached token's K and V rows (MLA: its 576-wide latent
+    row, read once for all heads), the queries, the outputs, and the block
+    table rows of a paged cache.  Split-K partials are implementation
+    overhead and are not counted.  FLOPs: 2 per multiply-add of the score and
+    attention-times-value products.
+    """
+    import numpy as np
+
+    ntok = int(np.sum(lens))
+    if hasattr(w, "num_kv_heads"):
+        eb = 4 if w.dtype == "f32" else 2
+        kv = 2 * w.num_kv_heads * w.head_dim * eb * ntok
+        qo = 2 * w.batch * w.num_q_heads * w.head_dim * eb
+        table = 4 * int(np.sum((lens + w.block_size - 1) // w.block_size)) if w.paged else 0
+        flops = 4 * w.num_q_heads * w.head_dim * ntok
+        return kv + qo + table, flops
+    width = w.d_latent + w.d_rope
+    kv = width * 2 * ntok
+    qo = w.batch * w.num_heads * (width + w.d_latent) * 2
+    table = 4 * int(np.sum((lens + w.block_size - 1) // w.block_size)) if w.paged else 0
+    flops = 2 * w.num_heads * (width + w.d_latent) * ntok
+    return kv + qo + table, flops
+
+
+def cpu_baseline(w, x, seconds):
+    """Time the fp64 oracle on whole sequences of the same inputs until `seconds` have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from decode_attention_kv_03_amd import workloads as W
+
+    lens = W.host_view(x["seq_lens"])
+    bf16 = w.dtype == "bf16"
+    q = W.host_view(x["q"])
+    done, t_total = 0, 0.0
+    order = np.random.default_rng(0).permutation(w.batch)
+    for b in order:
+        b = int(b)
+        if hasattr(w, "num_kv_heads"):
+            if w.paged:
+                bt = W.host_view(x["block_table"][b:b + 1])
+                nblk = (int(lens[b]) + w.block_size - 1) // w.block_size
+                ids = bt[0, :nblk]
+                k = W.host_view(x["k"][torch_index(ids, x["k"].device)])
+                v = W.host_view(x["v"][torch_index(ids, x["v"].device)])
+                tbl = np.arange(nblk, dtype=np.int64)[None]
+                t0 = time.perf_counter()
+                oracle.paged_gqa_decode(q[b:b + 1], k, v, tbl, lens[b:b + 1], w.block_size, w.scale, bf16=bf16)
+            else:
+                k = W.host_view(x["k"][b])[None]
+                v = W.host_view(x["v"][b])[None]
+                t0 = time.perf_counter()
+                oracle.gqa_decode(q[b:b + 1], k, v, lens[b:b + 1], w.scale, bf16=bf16)
+        else:
+            c = W.host_view(x["cache"][b])[None]
+            t0 = time.perf_counter()
+            oracle.mla_absorbed_decode(q[b:b + 1], c, lens[b:b + 1], w.scale, d_c=w.d_latent, bf16=bf16)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": done / t_total,
+        "unit": "seq-steps/s per layer",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.batch} sequences of {w.name}, fp64 NumPy oracle, one sequence per call "
+                  f"(bf16->fp64 widening included), {t_total:.1f} s",
+    }
+
+
+def torch_index(ids, device):
+    import torch
+
+    return torch.from_numpy(ids.astype("int64")).to(device)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from decode_attention_kv_03_amd import gqa_decode, mla_decode, gqa_workspace_bytes, mla_workspace_bytes
+    from decode_attention_kv_03_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    is_gqa = hasattr(w, "num_kv_heads")
+    make = W.make_gqa_inputs if is_gqa else W.make_mla_inputs
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    x0 = make(w, dev)
+    lens = W.host_view(x0["seq_lens"])
+    nbytes, flops = algorithmic(w, lens)
+    cache_bytes = sum(t.numel() * t.element_size() for k, t in x0.items() if k in ("k", "v", "cache"))
+    copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(cache_bytes, 1))))
+    xs = [x0]
+    for c in range(1, copies):
+        xc = dict(x0)
+        for k in ("k", "v", "cache"):
+            if k in x0:
+                xc[k] = x0[k].clone()
+        xs.append(xc)
+
+    stream = torch.cuda.current_stream()
+    if is_gqa:
+        out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=x0["q"].dtype, device=dev)
+        max_len = w.seq_len
+        ws_n = gqa_workspace_bytes(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, w.block_size,
+                                   args.split_tokens, x0["q"].dtype)
+    else:
+        out = torch.empty((w.batch, w.num_heads, w.d_latent), dtype=x0["q"].dtype, device=dev)
+        max_len = w.seq_len
+        ws_n = mla_workspace_bytes(w.batch, w.num_heads, max_len, w.d_latent, w.d_rope, w.block_size,
+                                   args.split_tokens)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        x = xs[i % copies]
+        if is_gqa:
+            gqa_decode(x["q"], x["k"], x["v"], x["seq_lens"], w.scale, block_table=x["block_table"],
+                       max_seq_len=max_len, out=out, split_tokens=args.split_tokens, workspace=ws, stream=stream)
+        else:
+            mla_decode(x["q"], x["cache"], x["seq_lens"], w.scale, block_table=x["block_table"], max_seq_len=max_len,
+                       out=out, split_tokens=args.split_tokens, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
+
+    # Per-call HIP events on the stream the kernels run on, plus wall time around the whole loop.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = wall * 1e3 / args.steps
+    mean_call_s = float(call_ms.mean()) * 1e-3
+    value = w.batch / (ms_per_step * 1e-3)
+
+    achieved_gbs = nbytes / mean_call_s / 1e9
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "kernel": "decode call: split-K kernel + log-sum-exp merge",
+        "call_us_mean": round(mean_call_s * 1e6, 2),
+        "call_us_p10_p50_p90": [round(float(np.percentile(call_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
+        "algorithmic_bytes_per_call": int(nbytes),
+        "algorithmic_flops_per_call": int(flops),
+        "intensity_flop_per_byte": round(flops / nbytes, 2),
+    }
+    if not is_gqa:
+        roofline["mfma_tflops"] = round(flops / mean_call_s / 1e12, 1)
+        roofline["mfma_frac_of_bf16_peak"] = round(flops / mean_call_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU reference", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, x0, args.cpu_seconds)
+
+    cfg = {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "dtype": w.dtype,
+           "rotated_input_copies": copies, "split_tokens": args.split_tokens or "auto"}
+    if is_gqa:
+        cfg.update({"num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                    "block_size": w.block_size})
+    else:
+        cfg.update({"num_heads": w.num_heads, "d_latent": w.d_latent, "d_rope": w.d_rope, "block_size": w.block_size})
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "seq-steps/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1), rounded to the storage dtype)",
+        "config": cfg,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

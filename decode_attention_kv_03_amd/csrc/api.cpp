@@ -1,0 +1,304 @@
+// C ABI of libkvattn: argument checks, split planning and kernel dispatch.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// touches no device state.  The library never allocates, frees or
+// synchronises; it only enqueues kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "../../include/kvattn.h"
+#include "kvattn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvattn_status fail(kvattn_status s, const char* fmt, long long a = 0, long long b = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), fmt, a, b);
+  g_last_error = buf;
+  return s;
+}
+
+kvattn_status ok() {
+  g_last_error.clear();
+  return KVATTN_OK;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+constexpr int kCUs = 256;          // MI355X compute units
+constexpr int32_t kMaxGridYZ = 65535;  // largest y/z grid dimension the launches use
+
+// Tokens per split for GQA.  Aim for about four workgroups per CU over the
+// whole grid (assuming every sequence is max_seq_len long), never below the
+// size where per-split partials (r heads x 128 fp32, written and read back)
+// exceed ~1/16 of the split's K/V bytes, and never above 2048 so that ragged
+// lengths still balance.
+int32_t plan_gqa_split(int32_t batch, int32_t h, int32_t g, int32_t max_seq_len, int32_t requested) {
+  if (requested > 0) return requested;
+  const int64_t S = max_seq_len > 0 ? max_seq_len : 1;
+  const int64_t units = (int64_t)batch * g;
+  const int64_t r = h / g;
+  int64_t chunk = round_up((S * units + 4 * kCUs - 1) / (4 * kCUs), KVATTN_SPLIT_ALIGN);
+  const int64_t min_chunk = std::max<int64_t>(256, 16 * r);
+  chunk = std::max(chunk, min_chunk);
+  chunk = std::min<int64_t>(chunk, 2048);
+  chunk = std::min(chunk, round_up(S, KVATTN_SPLIT_ALIGN));
+  return (int32_t)chunk;
+}
+
+// Tokens per split for MLA: one 128-head workgroup fills a CU, so aim for
+// one workgroup per CU.
+int32_t plan_mla_split(int32_t batch, int32_t h, int32_t max_seq_len, int32_t requested) {
+  (void)h;
+  if (requested > 0) return requested;
+  const int64_t S = max_seq_len > 0 ? max_seq_len : 1;
+  int64_t chunk = round_up((S * batch + kCUs - 1) / kCUs, KVATTN_SPLIT_ALIGN);
+  chunk = std::max<int64_t>(chunk, 256);
+  chunk = std::min<int64_t>(chunk, 4096);
+  chunk = std::min(chunk, round_up(S, KVATTN_SPLIT_ALIGN));
+  return (int32_t)chunk;
+}
+
+int32_t n_splits(int32_t max_seq_len, int32_t split) {
+  if (max_seq_len <= split) return 1;
+  return (int32_t)((max_seq_len + split - 1) / split);
+}
+
+size_t partial_bytes(int64_t batch, int64_t heads, int64_t nsplit, int64_t d_v) {
+  if (nsplit <= 1) return 0;
+  return (size_t)(batch * heads * nsplit * (d_v + 1) * (int64_t)sizeof(float));
+}
+
+kvattn_status check_split(int32_t split_tokens) {
+  if (split_tokens < 0 || split_tokens % KVATTN_SPLIT_ALIGN != 0)
+    return fail(KVATTN_ERR_INVALID, "split_tokens must be 0 or a positive multiple of 64 (got %lld)", split_tokens);
+  return KVATTN_OK;
+}
+
+kvattn_status check_cache_geometry(int64_t cache_len, int32_t block_size, int32_t max_blocks, int32_t max_seq_len,
+                                   bool paged) {
+  if (max_seq_len < 0) return fail(KVATTN_ERR_INVALID, "max_seq_len must be >= 0 (got %lld)", max_seq_len);
+  if (cache_len < 1) return fail(KVATTN_ERR_INVALID, "cache_len must be >= 1 (got %lld)", cache_len);
+  if (!paged) {
+    if (max_seq_len > cache_len)
+      return fail(KVATTN_ERR_INVALID, "max_seq_len %lld exceeds the contiguous cache length %lld", max_seq_len,
+                  cache_len);
+    return KVATTN_OK;
+  }
+  if (block_size < 1) return fail(KVATTN_ERR_INVALID, "block_size must be >= 1 for a paged cache (got %lld)", block_size);
+  if (max_blocks < 1)
+    return fail(KVATTN_ERR_INVALID, "max_blocks_per_seq must be >= 1 for a paged cache (got %lld)", max_blocks);
+  if ((int64_t)max_seq_len > (int64_t)max_blocks * block_size)
+    return fail(KVATTN_ERR_INVALID, "max_seq_len %lld exceeds max_blocks_per_seq * block_size = %lld", max_seq_len,
+                (long long)max_blocks * block_size);
+  return KVATTN_OK;
+}
+
+kvattn_status check_gqa(const void* q, const void* k, const void* v, const int32_t* lens, const void* out,
+                        int32_t batch, int32_t h, int32_t g, int32_t d, kvattn_dtype dtype, float scale) {
+  if (!q || !k || !v || !lens || !out) return fail(KVATTN_ERR_INVALID, "q, k_cache, v_cache, seq_lens and out must be non-null");
+  if (batch < 1) return fail(KVATTN_ERR_INVALID, "batch must be >= 1 (got %lld)", batch);
+  if (h < 1 || g < 1) return fail(KVATTN_ERR_INVALID, "head counts must be >= 1 (h=%lld, g=%lld)", h, g);
+  if (h % g != 0) return fail(KVATTN_ERR_INVALID, "num_q_heads %lld is not a multiple of num_kv_heads %lld", h, g);
+  if (d < 1) return fail(KVATTN_ERR_INVALID, "head_dim must be >= 1 (got %lld)", d);
+  if (dtype != KVATTN_F32 && dtype != KVATTN_BF16) return fail(KVATTN_ERR_INVALID, "unknown dtype %lld", (int)dtype);
+  if (!std::isfinite(scale)) return fail(KVATTN_ERR_INVALID, "scale must be finite");
+  if (d != kvattn::kHeadDim) return fail(KVATTN_ERR_UNSUPPORTED, "head_dim %lld is not supported (only 128)", d);
+  if (batch > kMaxGridYZ || g > kMaxGridYZ)
+    return fail(KVATTN_ERR_UNSUPPORTED, "batch %lld and num_kv_heads %lld must be <= 65535", batch, g);
+  const int32_t r = h / g;
+  if (dtype == KVATTN_F32 && r > kvattn::kMaxGroupF32)
+    return fail(KVATTN_ERR_UNSUPPORTED, "fp32 supports h/g <= 64 (got %lld)", r);
+  if (dtype == KVATTN_BF16 && r > kvattn::kMaxGroupBf16)
+    return fail(KVATTN_ERR_UNSUPPORTED, "bf16 supports h/g <= 128 (got %lld)", r);
+  return KVATTN_OK;
+}
+
+kvattn_status check_mla(const void* q, const void* cache, const int32_t* lens, const void* out, int32_t batch,
+                        int32_t h, int32_t d_c, int32_t d_r, kvattn_dtype dtype, float scale) {
+  if (!q || !cache || !lens || !out) return fail(KVATTN_ERR_INVALID, "q, cache, seq_lens and out must be non-null");
+  if (batch < 1) return fail(KVATTN_ERR_INVALID, "batch must be >= 1 (got %lld)", batch);
+  if (h < 1) return fail(KVATTN_ERR_INVALID, "num_heads must be >= 1 (got %lld)", h);
+  if (d_c < 1 || d_r < 0) return fail(KVATTN_ERR_INVALID, "bad MLA widths d_latent=%lld d_rope=%lld", d_c, d_r);
+  if (dtype != KVATTN_F32 && dtype != KVATTN_BF16) return fail(KVATTN_ERR_INVALID, "unknown dtype %lld", (int)dtype);
+  if (!std::isfinite(scale)) return fail(KVATTN_ERR_INVALID, "scale must be finite");
+  if (d_c != kvattn::kMlaLatent || d_r != kvattn::kMlaRope)
+    return fail(KVATTN_ERR_UNSUPPORTED, "MLA supports d_latent=512, d_rope=64 (got %lld, %lld)", d_c, d_r);
+  if (dtype != KVATTN_BF16) return fail(KVATTN_ERR_UNSUPPORTED, "MLA supports bf16 only");
+  if (batch > kMaxGridYZ) return fail(KVATTN_ERR_UNSUPPORTED, "batch %lld must be <= 65535", batch);
+  if (h % 16 != 0 || h > kvattn::kMaxMlaHeads)
+    return fail(KVATTN_ERR_UNSUPPORTED, "MLA supports num_heads a multiple of 16 up to 128 (got %lld)", h);
+  return KVATTN_OK;
+}
+
+kvattn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return KVATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvattn_status_string(kvattn_status s) {
+  switch (s) {
+    case KVATTN_OK: return "ok";
+    case KVATTN_ERR_INVALID: return "invalid argument";
+    case KVATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVATTN_ERR_WORKSPACE: return "workspace too small";
+    case KVATTN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* kvattn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kvattn_gqa_split_tokens(int32_t batch, int32_t h, int32_t g, int32_t max_seq_len, int32_t block_size,
+                                int32_t split_tokens) {
+  (void)block_size;
+  if (batch < 1 || h < 1 || g < 1 || h % g != 0 || split_tokens < 0) return -1;
+  return plan_gqa_split(batch, h, g, max_seq_len, split_tokens);
+}
+
+int32_t kvattn_mla_split_tokens(int32_t batch, int32_t h, int32_t max_seq_len, int32_t block_size,
+                                int32_t split_tokens) {
+  (void)block_size;
+  if (batch < 1 || h < 1 || split_tokens < 0) return -1;
+  return plan_mla_split(batch, h, max_seq_len, split_tokens);
+}
+
+size_t kvattn_gqa_workspace_bytes(int32_t batch, int32_t h, int32_t g, int32_t d, int32_t max_seq_len,
+                                  int32_t block_size, int32_t split_tokens, kvattn_dtype dtype) {
+  (void)block_size;
+  (void)dtype;
+  if (batch < 1 || h < 1 || g < 1 || h % g != 0 || d < 1 || max_seq_len < 0 || split_tokens < 0 ||
+      split_tokens % KVATTN_SPLIT_ALIGN != 0)
+    return (size_t)-1;
+  const int32_t split = plan_gqa_split(batch, h, g, max_seq_len, split_tokens);
+  return partial_bytes(batch, h, n_splits(max_seq_len, split), d);
+}
+
+size_t kvattn_mla_workspace_bytes(int32_t batch, int32_t h, int32_t d_c, int32_t d_r, int32_t max_seq_len,
+                                  int32_t block_size, int32_t split_tokens, kvattn_dtype dtype) {
+  (void)block_size;
+  (void)dtype;
+  (void)d_r;
+  if (batch < 1 || h < 1 || d_c < 1 || max_seq_len < 0 || split_tokens < 0 || split_tokens % KVATTN_SPLIT_ALIGN != 0)
+    return (size_t)-1;
+  const int32_t split = plan_mla_split(batch, h, max_seq_len, split_tokens);
+  return partial_bytes(batch, h, n_splits(max_seq_len, split), d_c);
+}
+
+kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, void* out, float* lse, int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int64_t cache_len, int32_t block_size,
+                                int32_t max_blocks_per_seq, int32_t max_seq_len, float scale, kvattn_dtype dtype,
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  kvattn_status st = check_gqa(q, k_cache, v_cache, seq_lens, out, batch, num_q_heads, num_kv_heads, head_dim, dtype,
+                               scale);
+  if (st != KVATTN_OK) return st;
+  const bool paged = block_table != nullptr;
+  if ((st = check_cache_geometry(cache_len, block_size, max_blocks_per_seq, max_seq_len, paged)) != KVATTN_OK)
+    return st;
+  if ((st = check_split(split_tokens)) != KVATTN_OK) return st;
+
+  const int32_t split = plan_gqa_split(batch, num_q_heads, num_kv_heads, max_seq_len, split_tokens);
+  const int32_t nsplit = n_splits(max_seq_len, split);
+  const size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
+                workspace == nullptr ? 0 : (long long)workspace_bytes);
+
+  kvattn::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.cache_len = cache_len;
+  a.block_size = paged ? block_size : 0;
+  a.max_blocks = paged ? max_blocks_per_seq : 0;
+  a.len_cap = max_seq_len;
+  a.split_tokens = split;
+  a.n_split = nsplit;
+  a.scale_log2 = scale * kvattn::kLog2eHost;
+  if (nsplit > 1) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (int64_t)batch * num_q_heads * nsplit * head_dim;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == KVATTN_BF16 ? kvattn::launch_gqa_bf16(a, s) : kvattn::launch_gqa_f32(a, s);
+  if (e != hipSuccess) return hip_status(e, "split kernel launch");
+  if (nsplit > 1) {
+    e = kvattn::launch_merge(a, head_dim, dtype == KVATTN_BF16, s);
+    if (e != hipSuccess) return hip_status(e, "merge kernel launch");
+  }
+  return ok();
+}
+
+kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t* block_table, const int32_t* seq_lens,
+                                void* out, float* lse, int32_t batch, int32_t num_heads, int32_t d_latent,
+                                int32_t d_rope, int64_t cache_len, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t max_seq_len, float scale, kvattn_dtype dtype, int32_t split_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  kvattn_status st = check_mla(q, cache, seq_lens, out, batch, num_heads, d_latent, d_rope, dtype, scale);
+  if (st != KVATTN_OK) return st;
+  const bool paged = block_table != nullptr;
+  if ((st = check_cache_geometry(cache_len, block_size, max_blocks_per_seq, max_seq_len, paged)) != KVATTN_OK)
+    return st;
+  if ((st = check_split(split_tokens)) != KVATTN_OK) return st;
+
+  const int32_t split = plan_mla_split(batch, num_heads, max_seq_len, split_tokens);
+  const int32_t nsplit = n_splits(max_seq_len, split);
+  const size_t need = partial_bytes(batch, num_heads, nsplit, d_latent);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
+                workspace == nullptr ? 0 : (long long)workspace_bytes);
+
+  kvattn::DecodeArgs a{};
+  a.q = q;
+  a.k = cache;
+  a.v = nullptr;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.num_q_heads = num_heads;
+  a.num_kv_heads = 1;
+  a.group = num_heads;
+  a.cache_len = cache_len;
+  a.block_size = paged ? block_size : 0;
+  a.max_blocks = paged ? max_blocks_per_seq : 0;
+  a.len_cap = max_seq_len;
+  a.split_tokens = split;
+  a.n_split = nsplit;
+  a.scale_log2 = scale * kvattn::kLog2eHost;
+  if (nsplit > 1) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (int64_t)batch * num_heads * nsplit * d_latent;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = kvattn::launch_mla_bf16(a, s);
+  if (e != hipSuccess) return hip_status(e, "MLA kernel launch");
+  if (nsplit > 1) {
+    e = kvattn::launch_merge(a, d_latent, true, s);
+    if (e != hipSuccess) return hip_status(e, "merge kernel launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

