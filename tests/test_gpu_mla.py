@@ -1,0 +1,123 @@
+"""GPU parity of kvattn_mla_decode (through the C ABI) against the fp64 oracle.
+
+bf16 inputs: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_03_amd import mla_decode
+from decode_attention_kv_03_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ATOL, RTOL = 2e-2, 1e-2
+
+
+def setup_module(_):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def note(msg):
+    print(f"\n[gpu-test] {msg}", flush=True)
+
+
+def assert_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside tolerance, max abs err {err.max():.3e}"
+
+
+def reference(x, rows=None):
+    w = x["workload"]
+    q = W.host_view(x["q"])
+    lens = W.host_view(x["seq_lens"])
+    if rows is None:
+        rows = list(range(w.batch))
+    if w.paged:
+        return oracle.paged_mla_absorbed_decode(q[rows], W.host_view(x["cache"]), W.host_view(x["block_table"])[rows],
+                                                lens[rows], w.block_size, w.scale, d_c=w.d_latent, bf16=True)
+    c = np.stack([W.host_view(x["cache"][b]) for b in rows])
+    return oracle.mla_absorbed_decode(q[rows], c, lens[rows], w.scale, d_c=w.d_latent, bf16=True)
+
+
+def run(x, **kw):
+    w = x["workload"]
+    out, lse = mla_decode(x["q"], x["cache"], x["seq_lens"], w.scale, block_table=x["block_table"],
+                          return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+CASES = [
+    # B, h, lens, split
+    (1, 128, [1], 0),
+    (2, 128, [31, 33], 0),
+    (2, 128, [32, 64], 64),
+    (3, 128, [100, 1, 65], 64),
+    (2, 64, [1000, 999], 256),
+    (2, 16, [300, 17], 128),
+    (2, 128, [2049, 777], 0),
+    (1, 128, [96], 64),
+]
+
+
+@pytest.mark.parametrize("B,h,lens,split", CASES)
+def test_contiguous_ragged_with_poisoned_tail(B, h, lens, split):
+    w = W.MlaWorkload(f"mla_{B}_{h}", B, h, max(lens) + 5, 500 + h + B, 1 / np.sqrt(192))
+    note(f"mla B={B} h={h} lens={lens} split={split}")
+    x = W.make_mla_inputs(w, DEV, lens=lens, poison_tail=True)
+    ref, ref_lse = reference(x)
+    out, lse = run(x, split_tokens=split)
+    assert_close(out.float().cpu().numpy(), ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+
+
+def test_zero_lengths():
+    w = W.MlaWorkload("mla_zero", 3, 128, 64, 8, 0.1)
+    note("mla zero lengths")
+    x = W.make_mla_inputs(w, DEV, lens=[0, 64, 0])
+    for split in (0, 64):
+        out, lse = run(x, split_tokens=split)
+        o = out.float().cpu().numpy()
+        assert np.all(o[0] == 0) and np.all(o[2] == 0)
+        assert np.all(np.isneginf(lse.cpu().numpy()[[0, 2]]))
+        ref, _ = reference(x, rows=[1])
+        assert_close(o[1:2], ref)
+
+
+@pytest.mark.parametrize("bs", [16, 5, 64])
+def test_paged(bs):
+    w = W.MlaWorkload(f"mla_paged_bs{bs}", 4, 128, 400, 40 + bs, 1 / np.sqrt(192), block_size=bs)
+    note(f"mla paged bs={bs}")
+    x = W.make_mla_inputs(w, DEV, poison_tail=True)
+    ref, _ = reference(x)
+    for split in (0, 64):
+        out, _ = run(x, split_tokens=split)
+        assert_close(out.float().cpu().numpy(), ref, f"split={split}")
+
+
+def test_rerun_is_bit_identical():
+    w = W.shrink(W.WORKLOADS["deepseek_v2_mla_h128_b32_s8192"], batch=4, seq_len=3000)
+    note("mla determinism")
+    x = W.make_mla_inputs(w, DEV)
+    a, la = run(x)
+    b, lb = run(x)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_full_size_sampled():
+    w = W.WORKLOADS["deepseek_v2_mla_h128_b32_s8192"]
+    note(w.name)
+    x = W.make_mla_inputs(w, DEV)
+    out, lse = run(x)
+    rows = [0, 13, 31]
+    ref, ref_lse = reference(x, rows=rows)
+    assert_close(out[rows].float().cpu().numpy(), ref, w.name)
+    np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    assert torch.isfinite(out.float()).all()
