@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="instead of the workload, run a plain device copy of BYTES bytes --steps times "
+                        "(reference kernel for scaling HBM traffic counters)")
     return p.parse_args()
 
 
@@ -133,6 +136,16 @@ def main():
 
     from decode_attention_kv_03_amd import gqa_decode, mla_decode, gqa_workspace_bytes, mla_workspace_bytes
     from decode_attention_kv_03_amd import workloads as W
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": args.steps}), flush=True)
+        return
 
     w = W.WORKLOADS[args.workload]
     dev = "cuda:0"

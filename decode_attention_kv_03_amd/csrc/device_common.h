@@ -11,28 +11,46 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Round-to-nearest-even float -> bfloat16 bit pattern (NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
 // 2^x on the hardware exp unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
+// Max over lanes {l, l^16, l^32, l^48}: the gfx950 row swaps exchange
+// 16-lane rows (odd <-> even) and 32-lane halves on the VALU, so each pair
+// of results holds a lane's own value and its partner's.
+__device__ __forceinline__ float max_over_row_groups(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-__device__ __forceinline__ float wave_sum_xor(float v, int mask) { return v + __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ float sum_over_row_groups(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Two floats -> packed bfloat16 pair (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// Sum of the two bfloat16 values of a packed pair, added to acc in fp32.
+__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), ones, acc, false);
+}
 
 // Full 64-lane reductions.
 __device__ __forceinline__ float wave_reduce_max(float v) {

@@ -49,7 +49,8 @@ template <int HBW, int WH>
 __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
   static_assert(WH == 1 || HBW == 1, "token-split waves own one head block");
   const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave-derived values in SGPRs
   const int n16 = lane & 15, grp = lane >> 4;
   const int r = a.group, h = a.num_q_heads;
 
@@ -150,21 +151,15 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
           const int tok = t0 + row0 + 4 * grp + v;
           sv[v] = tok < t_end ? s[v] * a.scale_log2 : -INFINITY;
         }
-        float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        mt = wave_max_xor(mt, 16);
-        mt = wave_max_xor(mt, 32);
+        const float mt = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
         const float m_new = fmaxf(m_run[hbi], mt);
         const float alpha = fast_exp2(m_run[hbi] - m_new);
         m_run[hbi] = m_new;
-        uint16_t pb16[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          pb16[v] = f32_to_bf16_bits(fast_exp2(sv[v] - m_new));
-          psum += bf16_bits_to_f32(pb16[v]);  // normalise with the weights the matrix core sees
-        }
-        l_run[hbi] = l_run[hbi] * alpha + psum;
-        const i16x4 pb = {(short)pb16[0], (short)pb16[1], (short)pb16[2], (short)pb16[3]};
+        const uint32_t p01 = pack_bf16x2(fast_exp2(sv[0] - m_new), fast_exp2(sv[1] - m_new));
+        const uint32_t p23 = pack_bf16x2(fast_exp2(sv[2] - m_new), fast_exp2(sv[3] - m_new));
+        // normalise with the weights the matrix core sees
+        l_run[hbi] = add_bf16x2(p23, add_bf16x2(p01, l_run[hbi] * alpha));
+        const i16x4 pb = __builtin_bit_cast(i16x4, (uint2){p01, p23});
         // Transpose-read rows (token) row0+4*grp .. +3, 16 columns per read:
         // lane n of a 16-lane group addresses row n/4, columns 4*(n%4)..+3 and
         // receives column n of the four rows.
@@ -183,10 +178,7 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
 
   // Per-head sums: the four lane groups hold different tokens of the same head.
 #pragma unroll
-  for (int hbi = 0; hbi < HBW; ++hbi) {
-    l_run[hbi] = wave_sum_xor(l_run[hbi], 16);
-    l_run[hbi] = wave_sum_xor(l_run[hbi], 32);
-  }
+  for (int hbi = 0; hbi < HBW; ++hbi) l_run[hbi] = sum_over_row_groups(l_run[hbi]);
 
   if constexpr (WH > 1) {
     // Waves that split the tile's tokens merge (max, sum, accumulator) through LDS.
@@ -233,8 +225,8 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + row * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const uint32_t lo = f32_to_bf16_bits(acc[hbi][db][0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[hbi][db][1] * inv) << 16);
-        const uint32_t hi = f32_to_bf16_bits(acc[hbi][db][2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[hbi][db][3] * inv) << 16);
+        const uint32_t lo = pack_bf16x2(acc[hbi][db][0] * inv, acc[hbi][db][1] * inv);
+        const uint32_t hi = pack_bf16x2(acc[hbi][db][2] * inv, acc[hbi][db][3] * inv);
         *reinterpret_cast<uint2*>(o + 16 * db + 4 * grp) = make_uint2(lo, hi);
       }
       if (a.lse != nullptr && grp == 0) a.lse[row] = lse2 * kLn2;

@@ -45,8 +45,8 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
     acc *= inv;
     if constexpr (BF16_OUT) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + row * DV + 4 * d4;
-      const uint32_t lo = f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
-      const uint32_t hi = f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+      const uint32_t lo = pack_bf16x2(acc[0], acc[1]);
+      const uint32_t hi = pack_bf16x2(acc[2], acc[3]);
       *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
     } else {
       *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * DV + 4 * d4) = acc;

@@ -84,8 +84,15 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
   constexpr int kWaves = 2 * 8 / HBW;
   constexpr int kDmaPer = kTileInsts / kWaves, kDmaExtra = kTileInsts % kWaves;
   static_assert(kWaves * HBW * 16 * 4 * 4 <= kSxBytes / 16 * 16, "score exchange must fit");
-  const int split = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // 1-D grid, XCD-aware: workgroup w runs on XCD w % 8, and every split of
+  // sequence b gets an id with the same residue, so a sequence's queries and
+  // partials stay in one XCD's L2.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int split = slot % a.n_split;
+  const int b = (slot / a.n_split) * 8 + xcd;
+  if (b >= a.batch) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave-derived values in SGPRs
   const int n16 = lane & 15, grp = lane >> 4;
   const int pair = wave >> 1, half = wave & 1;
   const int h = a.num_q_heads;
@@ -238,27 +245,27 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
       __builtin_amdgcn_sched_barrier(0);
     }
     // Swap partial scores with the other wave of the pair.
-    float* mine = sx + wave * (8 * HBW) * 64;
-    const float* other = sx + (wave ^ 1) * (8 * HBW) * 64;
+    // Each lane stores its four-score fragments as 16-byte words, consecutive
+    // across lanes.
+    f32x4* mine = reinterpret_cast<f32x4*>(sx) + wave * (2 * HBW) * 64;
+    const f32x4* other = reinterpret_cast<const f32x4*>(sx) + (wave ^ 1) * (2 * HBW) * 64;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int hbi = 0; hbi < HBW; ++hbi)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) mine[((st * HBW + hbi) * 4 + v) * 64 + lane] = s[st][hbi][v];
+      for (int hbi = 0; hbi < HBW; ++hbi) mine[(st * HBW + hbi) * 64 + lane] = s[st][hbi];
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int hbi = 0; hbi < HBW; ++hbi)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          // Add in a fixed order (lower half first) so both waves get identical sums.
-          const float o = other[((st * HBW + hbi) * 4 + v) * 64 + lane];
-          s[st][hbi][v] = half == 0 ? s[st][hbi][v] + o : o + s[st][hbi][v];
-        }
+      for (int hbi = 0; hbi < HBW; ++hbi) {
+        // Add in a fixed order (lower half first) so both waves get identical sums.
+        const f32x4 o = other[(st * HBW + hbi) * 64 + lane];
+        s[st][hbi] = half == 0 ? s[st][hbi] + o : o + s[st][hbi];
+      }
 
-    // Online softmax; P^T packed straight into the B-operand layout.
+    // Online softmax; P^T packed straight into the B-operand layout.  Only the
+    // last tile of a split can hold tokens past its end.
+    const bool ragged = t0 + kT > t_end;
     bf16x8 pp[HBW];
 #pragma unroll
     for (int hbi = 0; hbi < HBW; ++hbi) {
@@ -266,15 +273,14 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = t0 + 16 * st + 4 * grp + v;
-          sv[4 * st + v] = tok < t_end ? s[st][hbi][v] * a.scale_log2 : -INFINITY;
-        }
-      float mt = sv[0];
+        for (int v = 0; v < 4; ++v) sv[4 * st + v] = s[st][hbi][v] * a.scale_log2;
+      if (ragged) {
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
-      mt = wave_max_xor(mt, 16);
-      mt = wave_max_xor(mt, 32);
+        for (int e = 0; e < 8; ++e)
+          if (t0 + 16 * (e >> 2) + 4 * grp + (e & 3) >= t_end) sv[e] = -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mt = max_over_row_groups(mt);
       const bool need = mt > m_ref[hbi] + kRescaleSlack;  // also true while m_ref is -inf
       if (__any(need)) {
         const float m_new = need ? mt : m_ref[hbi];
@@ -284,17 +290,12 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
 #pragma unroll
         for (int db = 0; db < kDBHalf; ++db) acc[hbi][db] *= alpha;
       }
-      uint16_t pb[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[e] = f32_to_bf16_bits(fast_exp2(sv[e] - m_ref[hbi]));
-        psum += bf16_bits_to_f32(pb[e]);
-      }
-      l_run[hbi] += psum;
       u32x4 packed;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) packed[e] = (uint32_t)pb[2 * e] | ((uint32_t)pb[2 * e + 1] << 16);
+      for (int e = 0; e < 4; ++e) {
+        packed[e] = pack_bf16x2(fast_exp2(sv[2 * e] - m_ref[hbi]), fast_exp2(sv[2 * e + 1] - m_ref[hbi]));
+        l_run[hbi] = add_bf16x2(packed[e], l_run[hbi]);  // normalise with the weights the matrix core sees
+      }
       pp[hbi] = __builtin_bit_cast(bf16x8, packed);
     }
 
@@ -332,8 +333,7 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
   for (int hbi = 0; hbi < HBW; ++hbi) {
     const int head = (HBW * pair + hbi) * 16 + n16;
     if (head >= h) continue;
-    float l = wave_sum_xor(l_run[hbi], 16);
-    l = wave_sum_xor(l, 32);
+    const float l = sum_over_row_groups(l_run[hbi]);
     const int64_t row = (int64_t)b * h + head;
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
@@ -344,8 +344,8 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
 #pragma unroll
       for (int db = 0; db < kDBHalf; ++db) {
         const int start = 64 * (db >> 1) + 16 * (db & 1);
-        const uint32_t lo = f32_to_bf16_bits(acc[hbi][db][0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[hbi][db][1] * inv) << 16);
-        const uint32_t hi = f32_to_bf16_bits(acc[hbi][db][2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[hbi][db][3] * inv) << 16);
+        const uint32_t lo = pack_bf16x2(acc[hbi][db][0] * inv, acc[hbi][db][1] * inv);
+        const uint32_t hi = pack_bf16x2(acc[hbi][db][2] * inv, acc[hbi][db][3] * inv);
         *reinterpret_cast<uint2*>(o + start) = make_uint2(lo, hi);
       }
       if (a.lse != nullptr && grp == 0 && half == 0) a.lse[row] = lse2 * kLn2;
@@ -363,7 +363,8 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
 
 hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_q_heads % 16 != 0 || a.num_q_heads > kMaxMlaHeads) return hipErrorInvalidValue;
-  const dim3 grid(a.n_split, a.batch);
+  const int seq_groups = (a.batch + 7) / 8;
+  const dim3 grid(8 * seq_groups * a.n_split);
   mla_split_bf16<2><<<grid, dim3(512), 0, stream>>>(a);
   return hipGetLastError();
 }
