@@ -120,6 +120,29 @@ def cpu_baseline(w, x, seconds):
     }
 
 
+def hbm_probe(torch, stream, nbytes=2 << 30):
+    """Measured read ceiling: the library's streaming-read probe over 2 GiB (beyond the 256 MB MALL)."""
+    from decode_attention_kv_03_amd import hbm_read_probe
+
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    best = (0.0, 0)
+    for wgs in (1024, 2048, 4096):
+        for _ in range(3):
+            hbm_read_probe(buf, wgs, sink, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(10):
+            hbm_read_probe(buf, wgs, sink, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        gbs = 10 * nbytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+        best = max(best, (gbs, wgs))
+    del buf
+    return {"gbs": round(best[0], 1), "workgroups": best[1], "bytes": nbytes,
+            "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
+
+
 def torch_index(ids, device):
     import torch
 
@@ -167,6 +190,7 @@ def main():
         xs.append(xc)
 
     stream = torch.cuda.current_stream()
+    probe = hbm_probe(torch, stream)
     if is_gqa:
         out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=x0["q"].dtype, device=dev)
         max_len = w.seq_len
@@ -223,6 +247,8 @@ def main():
         "algorithmic_bytes_per_call": int(nbytes),
         "algorithmic_flops_per_call": int(flops),
         "intensity_flop_per_byte": round(flops / nbytes, 2),
+        "measured_read_ceiling_gbs": probe["gbs"],
+        "frac_of_measured_ceiling": round(achieved_gbs / probe["gbs"], 4),
     }
     if not is_gqa:
         roofline["mfma_tflops"] = round(flops / mean_call_s / 1e12, 1)
@@ -256,6 +282,7 @@ def main():
         "config": cfg,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "hbm_read_probe": probe,
     }
     print(json.dumps(line), flush=True)
 

@@ -20,6 +20,7 @@ from .kvattn import (  # noqa: F401
     KvattnError,
     gqa_decode,
     gqa_workspace_bytes,
+    hbm_read_probe,
     library_path,
     load_library,
     mla_decode,

@@ -301,4 +301,17 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
   return ok();
 }
 
+kvattn_status kvattn_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,
+                                    void* stream) {
+  if (!buf || !sink) return fail(KVATTN_ERR_INVALID, "buf and sink must be non-null");
+  if (bytes == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(KVATTN_ERR_INVALID, "bytes must be a positive multiple of 16 and buf 16-byte aligned (bytes=%lld)",
+                (long long)bytes);
+  if (workgroups < 1) return fail(KVATTN_ERR_INVALID, "workgroups must be >= 1 (got %lld)", workgroups);
+  hipError_t e = kvattn::launch_hbm_read_probe(buf, (int64_t)(bytes / 16), sink, workgroups,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "probe launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -107,8 +107,9 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
       if (t < t_end) {
         const int64_t off = cache_row_offset(a, b, j, t, kHeadDim);
         if (off >= 0) {
-          kv = *reinterpret_cast<const u32x4*>(kbase + off + col * 8);
-          vv = *reinterpret_cast<const u32x4*>(vbase + off + col * 8);
+          // read-once stream: non-temporal loads
+          kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off + col * 8));
+          vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off + col * 8));
         }
       }
       kst[u] = kv;

@@ -47,6 +47,7 @@ struct DecodeArgs {
 hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_hbm_read_probe(const void* buf, int64_t n16, uint32_t* sink, int workgroups, hipStream_t stream);
 // Log-sum-exp merge of the per-split partials into out/lse; d_v = 128 or 512.
 hipError_t launch_merge(const DecodeArgs& a, int d_v, bool out_bf16, hipStream_t stream);
 

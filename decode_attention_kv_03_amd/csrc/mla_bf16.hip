@@ -64,13 +64,15 @@ constexpr float kRescaleSlack = 8.f;        // log2 units
 __device__ __forceinline__ int swz(int row) { return (((row >> 1) & 3) << 1) | ((row >> 3) & 1); }
 
 // 16-byte global -> LDS copy of every lane: lane i's bytes land at
-// lds_base + 16 * i (lds_base is wave-uniform, taken through M0).  Issued as
+// lds_base + 16 * i (lds_base is wave-uniform, taken through M0).  The
+// non-temporal hint marks the cache stream as read-once, which measurably
+// raises the streaming rate on this part.  Issued as
 // inline assembly so the compiler does not treat every later LDS read as a
 // possible alias of the copy and drain all copies in flight; completion is
 // awaited explicitly with vmcnt before the tile is read.  M0 is written here
 // and nowhere else in this kernel.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");

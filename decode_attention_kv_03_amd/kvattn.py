@@ -36,6 +36,7 @@ SIGNATURES = {
     "kvattn_mla_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_gqa_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_mla_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "kvattn_hbm_read_probe": (_c_i32, [_c_vp, _c_sz, _c_vp, _c_i32, _c_vp]),
     "kvattn_status_string": (ctypes.c_char_p, [_c_i32]),
     "kvattn_last_error": (ctypes.c_char_p, []),
 }
@@ -109,6 +110,14 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def hbm_read_probe(buf, workgroups, sink, stream=None):
+    """Stream every byte of the GPU tensor `buf` once (measurement utility; see kvattn_hbm_read_probe)."""
+    _need_gpu(buf, sink)
+    lib = load_library()
+    _check(lib.kvattn_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(workgroups),
+                                     _stream(stream)))
 
 
 def gqa_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0, split_tokens=0,
