@@ -201,7 +201,7 @@ def main():
         max_len = w.seq_len
         ws_n = mla_workspace_bytes(w.batch, w.num_heads, max_len, w.d_latent, w.d_rope, w.block_size,
                                    args.split_tokens)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device=dev)  # zero-filled once, as the ABI asks
 
     def step(i):
         x = xs[i % copies]

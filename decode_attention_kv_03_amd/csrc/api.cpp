@@ -31,6 +31,10 @@ kvattn_status ok() {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+#ifndef KVATTN_GQA_RING_DEPTH
+#define KVATTN_GQA_RING_DEPTH 2
+#endif
+
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int32_t kMaxGridYZ = 65535;  // largest y/z grid dimension the launches use
 
@@ -235,6 +239,7 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
   a.split_tokens = split;
   a.n_split = nsplit;
   a.scale_log2 = scale * kvattn::kLog2eHost;
+  a.ring_depth = KVATTN_GQA_RING_DEPTH;
   if (nsplit > 1) {
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = a.part_o + (int64_t)batch * num_q_heads * nsplit * head_dim;

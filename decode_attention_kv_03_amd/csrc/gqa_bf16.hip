@@ -8,26 +8,29 @@
 //
 // Work decomposition.  One workgroup (4 waves) owns one (sequence, KV head,
 // split) and walks the split's tokens in 64-token tiles:
-//  * the tile's K and V rows (64 x 128 bf16 each, contiguous in HBM for a
-//    contiguous cache, 16-token runs for a paged one) are fetched with
-//    coalesced 16-byte loads into registers one tile ahead, then written to
-//    LDS, so the HBM stream overlaps the math of the previous tile;
-//  * scores are S^T = K_tile * Q^T on v_mfma_f32_16x16x32_bf16: 16 tokens x 16
-//    query heads per matrix op, the K operand read from LDS (row = token,
-//    eight consecutive head-dim values per lane) and Q^T held in registers;
-//  * the online softmax runs in the matrix-core output layout: lane l owns
-//    query head l%16 and tokens 4*(l/16)..+3, so per-head max/sum need two
-//    cross-lane exchanges (xor 16, xor 32) and everything else is lane-local;
-//  * P V is accumulated as O^T = V^T * P^T on v_mfma_f32_16x16x16_bf16: the
-//    probabilities already sit in the B-operand layout, and V^T comes from
-//    the row-major V tile through the gfx950 LDS transpose read
-//    (ds_read_b64_tr_b16), one read per 16 head-dim columns;
-//  * waves split the tile's tokens when a group has at most 32 heads
-//    (each wave keeps its own max/sum/accumulator, merged through LDS at the
-//    end) and split the heads when it has more;
+//  * tiles stream from HBM straight into an NST-stage LDS ring with
+//    global_load_lds_dwordx4 carrying the non-temporal hint (the cache is
+//    read once per step); NST-1 tiles are in flight while one is consumed.
+//    The copies are issued as inline assembly and awaited with explicit
+//    vmcnt counts, so the compiler never drains them before an LDS read;
+//  * rows are stored unpadded (256 B) with their 16-byte chunks XOR-swizzled
+//    by row, which keeps both LDS read patterns below conflict-free;
+//  * a paged cache's block-table slice for the split is staged in LDS first,
+//    so per-row block lookups never wait on the vector-memory counter;
+//  * scores are S^T = K_tile * Q^T on v_mfma_f32_16x16x32_bf16 (16 tokens x 16
+//    query heads, K from LDS, Q^T fragments in registers);
+//  * the online softmax runs in the matrix-core output layout (lane l: query
+//    head l%16, tokens 4*(l/16)+v), with lazy rescaling: the reference max
+//    only moves when a tile's max exceeds it by more than 8 (log2 units);
+//  * P V is accumulated as O^T = V^T * P^T; V^T comes from the row-major V
+//    tile through the gfx950 LDS transpose read (ds_read_b64_tr_b16).  Waves
+//    that own 32 tokens of a tile use 16x16x32 MFMAs (two transpose reads
+//    per operand), waves that own 16 use 16x16x16;
+//  * waves split the tile's tokens when a group has at most 32 heads (each
+//    keeps its own max/sum/accumulator, merged through LDS at the end) and
+//    split the heads when it has more;
 //  * the split's result is either the final output (one split) or an fp32
 //    partial plus its log2-domain log-sum-exp for the merge kernel.
-#include "cache_addr.h"
 #include "device_common.h"
 #include "kvattn_internal.h"
 
@@ -36,21 +39,56 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTile = 64;                        // tokens per LDS tile
-constexpr int kKStride = kHeadDim + 8;           // LDS row pitch of K (bf16): 272 B, conflict-free row reads
-constexpr int kVStride = kHeadDim + 16;          // LDS row pitch of V (bf16): 288 B, conflict-free transpose reads
-constexpr int kLdsK = kTile * kKStride * 2;      // bytes
-constexpr int kLdsV = kTile * kVStride * 2;
-constexpr int kLdsBytes = kLdsK + kLdsV;         // 35840 B
-constexpr int kRedFloatsPerWave = 34 * 64;       // 32 accumulators + max + sum, per lane
-static_assert(4 * kRedFloatsPerWave * 4 <= kLdsBytes, "cross-wave merge must fit in the tile buffer");
+constexpr int kTile = 64;                   // tokens per tile
+constexpr int kRowB = kHeadDim * 2;         // 256 B per K or V row
+constexpr int kTileB = kTile * kRowB;       // 16 KiB per tensor and tile
+constexpr int kStageB = 2 * kTileB;         // K tile, then V tile
+constexpr int kTblSlots = 2304;             // block-table entries staged in LDS
+constexpr int kRedFloatsPerWave = 34 * 64;  // 32 accumulators + max + sum, per lane
+constexpr float kRescaleSlack = 8.f;        // log2 units
 
-template <int HBW, int WH>
-__global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
+// Chunk swizzle of a 256-byte row: XOR of the 4-bit chunk index.  Rows r and
+// r+16 share it; 16 consecutive rows get 16 distinct values and any 8
+// consecutive rows 8 distinct pairs, which is what the two read patterns need.
+__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+
+// 16-byte global -> LDS copy of every lane (lane i lands at lds_base + 16 i;
+// lds_base is wave-uniform and goes through M0), non-temporal.  Inline
+// assembly so later LDS reads are not treated as aliases of the copy; M0 is
+// written here and nowhere else in these kernels.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// Wait until at most `N` of this wave's copies are outstanding, then
+// synchronise the workgroup (LDS reads of every wave complete first).
+template <int N>
+__device__ __forceinline__ void wait_copies_and_sync() {
+  static_assert(N == 0 || N == 8 || N == 16, "copy counts come in tiles of 8");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int HBW, int WH, int NST>
+__global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeArgs a) {
   static_assert(WH == 1 || HBW == 1, "token-split waves own one head block");
-  const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  static_assert(NST >= 2 && NST <= 3, "ring depth");
+  constexpr int kUnit = WH == 4 ? 16 : 32;  // tokens a wave handles per step
+  // 1-D grid, XCD-aware: workgroup w runs on XCD w % 8 and all splits of one
+  // (sequence, KV head) group share a residue, so the group's queries are
+  // fetched into one XCD's L2.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int split = slot % a.n_split;
+  const int unit = (slot / a.n_split) * 8 + xcd;
+  if (unit >= a.batch * a.num_kv_heads) return;
+  const int b = unit / a.num_kv_heads, j = unit - b * a.num_kv_heads;
+
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave-derived values in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: wave-derived values in SGPRs
   const int n16 = lane & 15, grp = lane >> 4;
   const int r = a.group, h = a.num_q_heads;
 
@@ -59,14 +97,14 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
   const bool final_out = (a.n_split == 1);
   if (!final_out && t_begin >= len) return;  // the merge only reads splits that hold tokens
   const int t_end = min(len, t_begin + a.split_tokens);
+  const int ntok = t_end - t_begin;
+  const int n_tiles = ntok > 0 ? (ntok + kTile - 1) / kTile : 0;
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
-  uint16_t* ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem + kLdsK);
-  auto* vs_lds = (__attribute__((address_space(3))) uint16_t*)vs;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NST][kStageB];
+  __shared__ int tbl[kTblSlots];
 
   const int hb0 = (wave / WH) * HBW;  // first 16-head block of this wave
-  const int ts = wave % WH;           // this wave's token slot within the tile
+  const int ts = wave % WH;           // this wave's token slot within a tile
 
   // Q^T fragments: lane l holds head (block*16 + l%16), dims 32*kk + 8*(l/16) .. +7.
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * h + (int64_t)j * r) * kHeadDim;
@@ -82,11 +120,28 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
     }
   }
 
+  // Paged cache: stage this split's block-table entries in LDS (plain loads,
+  // before any copy is in flight).  A split whose slice exceeds the LDS table
+  // reloads a window when a tile needs entries past it.
+  const bool paged = a.block_size != 0;
+  const int bs = a.block_size;
+  const int32_t* table_row = paged ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
+  int win_first = 0;
+  auto load_window = [&](int first) {
+    const int last_needed = (t_end - 1) / bs;
+    const int count = min(kTblSlots, last_needed - first + 1);
+    for (int i = tid; i < count; i += 256) tbl[i] = table_row[first + i];
+    win_first = first;
+  };
+  if (paged && n_tiles > 0) load_window(t_begin / bs);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries and table land before any copy is issued
+  __syncthreads();
+
   f32x4 acc[HBW][8];
-  float m_run[HBW], l_run[HBW];
+  float m_ref[HBW], l_run[HBW];
 #pragma unroll
   for (int hbi = 0; hbi < HBW; ++hbi) {
-    m_run[hbi] = -INFINITY;
+    m_ref[hbi] = -INFINITY;
     l_run[hbi] = 0.f;
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[hbi][db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -94,84 +149,133 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
 
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k);
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v);
-  u32x4 kst[4], vst[4];
-  // Thread tid fetches 16-byte chunks tid, tid+256, .. of the 64x256-byte tile:
-  // four consecutive rows per wave instruction, fully coalesced.
-  auto load_tile = [&](int t0) {
+  const int64_t head_rows = (int64_t)(b * a.num_kv_heads + j) * a.cache_len;  // contiguous: first row of (b, j)
+
+  // Copies of one tile: 32 wave instructions (16 for K, 16 for V) of 4 rows
+  // x 16 chunks; wave w issues instructions 8w .. 8w+7.  Lane l of
+  // instruction i writes LDS slot (row 4*(i%16) + l/16, chunk l%16), which
+  // holds logical chunk (l%16) ^ swz(row).  Rows past the split's end
+  // re-read its last row (masked out of the softmax).
+  auto issue_tile = [&](int t0, int stage) {
+    if (paged && (min(t0 + kTile, t_end) - 1) / bs >= win_first + kTblSlots) {
+      // slow path: slide the table window (drains the copies in flight)
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __syncthreads();
+      load_window(t0 / bs);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
+    const uint32_t stage_base = (uint32_t)(uintptr_t)&ring[stage][0];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + 256 * u;
-      const int row = c >> 4, col = c & 15;
-      const int t = t0 + row;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (t < t_end) {
-        const int64_t off = cache_row_offset(a, b, j, t, kHeadDim);
-        if (off >= 0) {
-          // read-once stream: non-temporal loads
-          kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off + col * 8));
-          vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off + col * 8));
-        }
+    for (int u = 0; u < 8; ++u) {
+      const int inst = wave * 8 + u;
+      const int tensor = inst >> 4, rg = inst & 15;
+      const int row = 4 * rg + (lane >> 4);
+      const int chunk = (lane & 15) ^ swz(row);
+      const int t = min(t0 + row, t_end - 1);
+      int64_t off;
+      if (!paged) {
+        off = (head_rows + t) * kHeadDim;
+      } else {
+        const int q = t / bs;
+        const int blk = tbl[q - win_first];
+        off = (blk >= 0 && (int64_t)blk < a.cache_len)
+                  ? (((int64_t)blk * a.num_kv_heads + j) * bs + (t - q * bs)) * kHeadDim
+                  : 0;  // out-of-range entry: an in-bounds stand-in row
       }
-      kst[u] = kv;
-      vst[u] = vv;
+      const uint16_t* src = (tensor == 0 ? kbase : vbase) + off + chunk * 8;
+      dma16(src, stage_base + tensor * kTileB + rg * 1024);
     }
   };
 
-  const int ntok = t_end - t_begin;
-  const int n_tiles = ntok > 0 ? (ntok + kTile - 1) / kTile : 0;
-  if (n_tiles > 0) load_tile(t_begin);
+  // Per-lane LDS byte offsets inside a tile.  K reads (A operand of the
+  // scores): row n16 of a 16-token subtile, chunk 4*kk + grp.  V transposing
+  // reads: rows 4*grp + (n16/4) (+16 per subtile), 8-byte piece n16%4 of the
+  // 16-column block db, i.e. chunk 2*db + (n16%4)/2.
+  int koff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = n16 * kRowB + 16 * ((4 * kk + grp) ^ swz(n16));
+  const int vrow = 4 * grp + (n16 >> 2);
+  int voff[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    voff[db] = kTileB + vrow * kRowB + 16 * ((2 * db + ((n16 & 3) >> 1)) ^ swz(vrow)) + 8 * (n16 & 1);
+
+  for (int s = 0; s < NST - 1 && s < n_tiles; ++s) issue_tile(t_begin + s * kTile, s);
 
   for (int it = 0; it < n_tiles; ++it) {
-    const int t0 = t_begin + it * kTile;
-    __syncthreads();  // every wave is done with the previous tile
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + 256 * u;
-      const int row = c >> 4, col = c & 15;
-      *reinterpret_cast<u32x4*>(ks + row * kKStride + col * 8) = kst[u];
-      *reinterpret_cast<u32x4*>(vs + row * kVStride + col * 8) = vst[u];
-    }
-    __syncthreads();
-    if (it + 1 < n_tiles) load_tile(t0 + kTile);  // in flight during this tile's math
+    // Tile `it` must have landed; the ones issued after it may stay in flight.
+    const int ahead = min(NST - 2, n_tiles - 1 - it);
+    if (ahead >= 2) wait_copies_and_sync<16>();
+    else if (ahead == 1) wait_copies_and_sync<8>();
+    else wait_copies_and_sync<0>();
+    if (it + NST - 1 < n_tiles) issue_tile(t_begin + (it + NST - 1) * kTile, (it + NST - 1) % NST);
 
-    for (int st = ts; st < 4; st += WH) {
-      const int row0 = st * 16;
-      if (t0 + row0 >= t_end) break;
+    const int t0 = t_begin + it * kTile;
+    const unsigned char* stage = ring[it % NST];
+    const auto* stage_lds = (const __attribute__((address_space(3))) unsigned char*)stage;
+
+    for (int u0 = ts * kUnit; u0 < kTile; u0 += WH * kUnit) {
+      if (t0 + u0 >= t_end) break;
+      constexpr int kSub = kUnit / 16;
 #pragma unroll
       for (int hbi = 0; hbi < HBW; ++hbi) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        f32x4 s[kSub];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const u32x4 kraw = *reinterpret_cast<const u32x4*>(ks + (row0 + n16) * kKStride + 32 * kk + 8 * grp);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kraw), qf[hbi][kk], s, 0, 0, 0);
-        }
-        // s[v] = q(head n16) . k(token t0 + row0 + 4*grp + v)
-        float sv[4];
+        for (int sb = 0; sb < kSub; ++sb) {
+          s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = t0 + row0 + 4 * grp + v;
-          sv[v] = tok < t_end ? s[v] * a.scale_log2 : -INFINITY;
+          for (int kk = 0; kk < 4; ++kk) {
+            const u32x4 kraw = *reinterpret_cast<const u32x4*>(stage + (u0 + 16 * sb) * kRowB + koff[kk]);
+            s[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kraw), qf[hbi][kk], s[sb],
+                                                            0, 0, 0);
+          }
         }
-        const float mt = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-        const float m_new = fmaxf(m_run[hbi], mt);
-        const float alpha = fast_exp2(m_run[hbi] - m_new);
-        m_run[hbi] = m_new;
-        const uint32_t p01 = pack_bf16x2(fast_exp2(sv[0] - m_new), fast_exp2(sv[1] - m_new));
-        const uint32_t p23 = pack_bf16x2(fast_exp2(sv[2] - m_new), fast_exp2(sv[3] - m_new));
-        // normalise with the weights the matrix core sees
-        l_run[hbi] = add_bf16x2(p23, add_bf16x2(p01, l_run[hbi] * alpha));
-        const i16x4 pb = __builtin_bit_cast(i16x4, (uint2){p01, p23});
-        // Transpose-read rows (token) row0+4*grp .. +3, 16 columns per read:
-        // lane n of a 16-lane group addresses row n/4, columns 4*(n%4)..+3 and
-        // receives column n of the four rows.
-        const int vrow = row0 + 4 * grp + (n16 >> 2);
-        const int vcol = 4 * (n16 & 3);
+        // s[sb][v] = q(head n16) . k(token t0 + u0 + 16*sb + 4*grp + v)
+        float sv[4 * kSub];
+#pragma unroll
+        for (int sb = 0; sb < kSub; ++sb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sv[4 * sb + v] = s[sb][v] * a.scale_log2;
+        if (t0 + u0 + kUnit > t_end) {
+#pragma unroll
+          for (int e = 0; e < 4 * kSub; ++e)
+            if (t0 + u0 + 16 * (e >> 2) + 4 * grp + (e & 3) >= t_end) sv[e] = -INFINITY;
+        }
+        float mt = sv[0];
+#pragma unroll
+        for (int e = 1; e < 4 * kSub; ++e) mt = fmaxf(mt, sv[e]);
+        mt = max_over_row_groups(mt);
+        const bool need = mt > m_ref[hbi] + kRescaleSlack;  // also true while m_ref is -inf
+        if (__any(need)) {
+          const float m_new = need ? mt : m_ref[hbi];
+          const float alpha = fast_exp2(m_ref[hbi] - m_new);
+          m_ref[hbi] = m_new;
+          l_run[hbi] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) acc[hbi][db] *= alpha;
+        }
+        uint32_t pk[2 * kSub];
+#pragma unroll
+        for (int e = 0; e < 2 * kSub; ++e) {
+          pk[e] = pack_bf16x2(fast_exp2(sv[2 * e] - m_ref[hbi]), fast_exp2(sv[2 * e + 1] - m_ref[hbi]));
+          l_run[hbi] = add_bf16x2(pk[e], l_run[hbi]);  // normalise with the weights the matrix core sees
+        }
+        const int vbase_off = u0 * kRowB;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          acc[hbi][db] *= alpha;
-          const i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vs_lds + vrow * kVStride + 16 * db + vcol));
-          acc[hbi][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb, acc[hbi][db], 0, 0, 0);
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage_lds + vbase_off + voff[db]));
+          if constexpr (kSub == 1) {
+            const i16x4 pb = __builtin_bit_cast(i16x4, (uint2){pk[0], pk[1]});
+            acc[hbi][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, pb, acc[hbi][db], 0, 0, 0);
+          } else {
+            // second 16 tokens of the unit: slots 4..7 of the 32-deep operand
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(stage_lds + vbase_off + 16 * kRowB + voff[db]));
+            const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){pk[0], pk[1], pk[2], pk[3]});
+            acc[hbi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[hbi][db], 0, 0, 0);
+          }
         }
       }
     }
@@ -184,13 +288,13 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
   if constexpr (WH > 1) {
     // Waves that split the tile's tokens merge (max, sum, accumulator) through LDS.
     __syncthreads();
-    float* red = reinterpret_cast<float*>(smem);
+    float* red = reinterpret_cast<float*>(&ring[0][0]);
     float* mine = red + wave * kRedFloatsPerWave;
 #pragma unroll
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int v = 0; v < 4; ++v) mine[(db * 4 + v) * 64 + lane] = acc[0][db][v];
-    mine[32 * 64 + lane] = m_run[0];
+    mine[32 * 64 + lane] = m_ref[0];
     mine[33 * 64 + lane] = l_run[0];
     __syncthreads();
     if (ts != 0) return;
@@ -199,16 +303,16 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
       const float* other = red + (wave + w2) * kRedFloatsPerWave;
       const float m2 = other[32 * 64 + lane];
       const float l2 = other[33 * 64 + lane];
-      const float M = fmaxf(m_run[0], m2);
+      const float M = fmaxf(m_ref[0], m2);
       if (M == -INFINITY) continue;
-      const float a1 = fast_exp2(m_run[0] - M);
+      const float a1 = fast_exp2(m_ref[0] - M);
       const float a2 = fast_exp2(m2 - M);
 #pragma unroll
       for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[0][db][v] = acc[0][db][v] * a1 + other[(db * 4 + v) * 64 + lane] * a2;
       l_run[0] = l_run[0] * a1 + l2 * a2;
-      m_run[0] = M;
+      m_ref[0] = M;
     }
   }
 
@@ -221,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
     const float l = l_run[hbi];
     const bool empty = !(l > 0.f);
     const float inv = empty ? 0.f : 1.f / l;
-    const float lse2 = empty ? -INFINITY : m_run[hbi] + __log2f(l);
+    const float lse2 = empty ? -INFINITY : m_ref[hbi] + __log2f(l);
     if (final_out) {
       uint16_t* o = static_cast<uint16_t*>(a.out) + row * kHeadDim;
 #pragma unroll
@@ -240,24 +344,30 @@ __global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.n_split, a.num_kv_heads, a.batch);
+template <int NST>
+hipError_t launch_depth(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t units = (int64_t)a.batch * a.num_kv_heads;
+  const dim3 grid((unsigned)(8 * ((units + 7) / 8) * a.n_split));
   const dim3 block(256);
   const int head_blocks = (a.group + 15) / 16;
   if (head_blocks == 1) {
-    gqa_split_bf16<1, 4><<<grid, block, 0, stream>>>(a);
+    gqa_split_bf16<1, 4, NST><<<grid, block, 0, stream>>>(a);
   } else if (head_blocks == 2) {
-    gqa_split_bf16<1, 2><<<grid, block, 0, stream>>>(a);
+    gqa_split_bf16<1, 2, NST><<<grid, block, 0, stream>>>(a);
   } else if (head_blocks <= 4) {
-    gqa_split_bf16<1, 1><<<grid, block, 0, stream>>>(a);
+    gqa_split_bf16<1, 1, NST><<<grid, block, 0, stream>>>(a);
   } else if (head_blocks <= 8) {
-    gqa_split_bf16<2, 1><<<grid, block, 0, stream>>>(a);
+    gqa_split_bf16<2, 1, NST><<<grid, block, 0, stream>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream) {
+  return a.ring_depth == 3 ? launch_depth<3>(a, stream) : launch_depth<2>(a, stream);
 }
 
 }  // namespace kvattn

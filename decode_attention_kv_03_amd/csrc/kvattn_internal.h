@@ -42,6 +42,7 @@ struct DecodeArgs {
   int32_t split_tokens;     // tokens per split (multiple of 64)
   int32_t n_split;          // splits per sequence in the grid
   float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
+  int32_t ring_depth;       // bf16 GQA: LDS ring stages (2 or 3)
 };
 
 hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream);

@@ -144,7 +144,7 @@ def _workspace(nbytes, workspace, device):
     if nbytes == 0:
         return None
     if workspace is None:
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"kvattn: workspace needs {nbytes} bytes")
     return workspace

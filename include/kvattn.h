@@ -59,6 +59,9 @@
  *    beyond fp32 rounding order.  The workspace holds the per-split partial
  *    results; its size comes from the matching *_workspace_bytes() call with
  *    the same shape arguments, and may be 0 (then workspace may be NULL).
+ *    Its contents need no initialisation.  One workspace serves one call at
+ *    a time: calls that share it must be ordered (for example, on one
+ *    stream).
  */
 #ifndef KVATTN_H
 #define KVATTN_H

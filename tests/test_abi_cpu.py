@@ -100,7 +100,7 @@ def test_gqa_rejects_bad_arguments_before_touching_the_gpu(kw, status):
 def test_gqa_workspace_required_when_split():
     # 4096 tokens at split 256 means 16 splits: a workspace is required.
     need = lib.kvattn_gqa_workspace_bytes(2, 8, 2, 128, 4096, 0, 256, K.KVATTN_BF16)
-    assert need == 2 * 8 * 16 * 129 * 4
+    assert need == 2 * 8 * 16 * 129 * 4  # 16 splits of partial outputs and log-sum-exps
     assert gqa(cache_len=4096, maxlen=4096, split=256, ws=None, wsb=0) == K.KVATTN_ERR_WORKSPACE
     assert gqa(cache_len=4096, maxlen=4096, split=256, ws=P, wsb=need - 1) == K.KVATTN_ERR_WORKSPACE
     # a single split needs none

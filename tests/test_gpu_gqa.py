@@ -169,6 +169,29 @@ def test_paged_odd_block_size():
     assert_close(out.float().cpu().numpy(), ref, "bf16")
 
 
+def test_workspace_reuse_across_calls_and_shapes():
+    """One workspace reused across calls of different shapes gives the same answers."""
+    from decode_attention_kv_03_amd import gqa_workspace_bytes
+
+    note("workspace reuse")
+    big = W.shrink(W.WORKLOADS["llama3_70b_gqa_h64_g8_b64_s8192"], batch=6, seq_len=1500)
+    small = W.GqaWorkload("small", 2, 32, 8, 128, 700, "bf16", 77, 0.08)
+    xb = W.make_gqa_inputs(big, DEV, lens=[1500, 3, 999, 64, 1200, 700])
+    xs = W.make_gqa_inputs(small, DEV, lens=[700, 129])
+    n = max(gqa_workspace_bytes(6, 64, 8, 128, 1500, 0, 64), gqa_workspace_bytes(2, 32, 8, 128, 700, 0, 64))
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ref_b, _ = reference(xb)
+    ref_s, _ = reference(xs)
+    outs = []
+    for x, ref in ((xb, ref_b), (xs, ref_s), (xb, ref_b), (xs, ref_s), (xb, ref_b)):
+        w = x["workload"]
+        out = gqa_decode(x["q"], x["k"], x["v"], x["seq_lens"], w.scale, split_tokens=64, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out.float().cpu().numpy(), ref, "bf16")
+        outs.append(out)
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[0], outs[4]) and torch.equal(outs[1], outs[3])
+
+
 def test_rerun_is_bit_identical():
     w = W.shrink(W.WORKLOADS["llama3_8b_gqa_h32_g8_b16_s8192"], batch=4, seq_len=2048)
     note("determinism")
