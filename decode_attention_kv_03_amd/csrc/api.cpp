@@ -85,6 +85,14 @@ kvattn_status check_split(int32_t split_tokens) {
   return KVATTN_OK;
 }
 
+// log2(x) for a power of two x > 0, else -1.
+int32_t pow2_shift(int32_t x) {
+  if (x <= 0 || (x & (x - 1)) != 0) return -1;
+  int32_t s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
 kvattn_status check_cache_geometry(int64_t cache_len, int32_t block_size, int32_t max_blocks, int32_t max_seq_len,
                                    bool paged) {
   if (max_seq_len < 0) return fail(KVATTN_ERR_INVALID, "max_seq_len must be >= 0 (got %lld)", max_seq_len);
@@ -234,6 +242,7 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
   a.group = num_q_heads / num_kv_heads;
   a.cache_len = cache_len;
   a.block_size = paged ? block_size : 0;
+  a.block_shift = paged ? pow2_shift(block_size) : -1;
   a.max_blocks = paged ? max_blocks_per_seq : 0;
   a.len_cap = max_seq_len;
   a.split_tokens = split;
@@ -287,6 +296,7 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
   a.group = num_heads;
   a.cache_len = cache_len;
   a.block_size = paged ? block_size : 0;
+  a.block_shift = paged ? pow2_shift(block_size) : -1;
   a.max_blocks = paged ? max_blocks_per_seq : 0;
   a.len_cap = max_seq_len;
   a.split_tokens = split;

@@ -10,6 +10,7 @@ namespace kvattn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -35,6 +36,20 @@ __device__ __forceinline__ float sum_over_row_groups(float v) {
   const uint32_t u = __float_as_uint(v);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(v);
+  const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Max and sum over lanes {l, l^32}: the two lane halves that hold the two
+// row groups of a 32x32 matrix-core result.
+__device__ __forceinline__ float max_over_halves(float v) {
+  const uint32_t w = __float_as_uint(v);
+  const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+__device__ __forceinline__ float sum_over_halves(float v) {
   const uint32_t w = __float_as_uint(v);
   const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);

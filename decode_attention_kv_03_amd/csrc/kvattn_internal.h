@@ -37,6 +37,7 @@ struct DecodeArgs {
   int32_t group;            // h / g
   int64_t cache_len;        // contiguous: tokens per (b, j) row block; paged: number of blocks
   int32_t block_size;       // 0: contiguous
+  int32_t block_shift;      // paged: log2(block_size) when it is a power of two, else -1
   int32_t max_blocks;       // paged: block_table row length
   int32_t len_cap;          // device lengths are clamped to [0, len_cap]
   int32_t split_tokens;     // tokens per split (multiple of 64)

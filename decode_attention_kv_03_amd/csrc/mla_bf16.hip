@@ -8,35 +8,40 @@
 // the output stays in the 512-wide latent space.  Nothing is reconstructed
 // per head, so each cached byte leaves HBM once per decode step.
 //
-// Both products are dense contractions and run on v_mfma_f32_16x16x32_bf16:
-//   S^T[32 tok x 16 heads] = C_tile[32 x 576] * Q^T[576 x 16]   (per head block)
-//   O^T[512 x 16 heads]   += C_tile[:, :512]^T * P^T[32 x 16]
-// One workgroup (8 waves) owns one (sequence, split) and all heads.  Waves
-// come in pairs: pair p owns heads 32p .. 32p+31 (two 16-head blocks); the
-// two waves of a pair each take half of the 576-wide score reduction (their
-// half of the queries lives in registers), swap partial scores through LDS,
-// and then each accumulates half of the 512 latent output columns.  So every
-// wave holds 32 heads' worth of operands per LDS read (half the LDS traffic
-// of 16-head waves) with half the registers of a 32-head wave.
+// Both products are dense contractions and run on v_mfma_f32_32x32x16_bf16,
+// the shape that sustains the matrix cores' full bf16 rate on this part
+// (the 16x16x32 shape issues at well under half of it):
+//   S^T[32 tok x 32 heads] = C_tile[32 x 576] * Q^T[576 x 32]
+//   O^T[32 cols x 32 heads] += C_tile[:, cols]^T * P^T[32 tok x 32 heads]
+// A workgroup (8 waves, two per SIMD) owns one (sequence, split) and all
+// heads.  Waves pair up per 32-head block: each wave of a pair holds the
+// query for half of the 576 dims (18 reduction steps of 16) and the output
+// accumulators for half of the 512 latent columns (8 blocks of 32), which
+// keeps both under the 256 registers a wave has at two waves per SIMD.  The
+// pair swaps partial scores through LDS once per tile.
 //
 // Data movement.  Tiles of 32 cache rows (36 KiB) stream from HBM straight
-// into LDS with global_load_lds_dwordx4 (no register staging), three tiles
-// deep, so two tiles are in flight while one is consumed.  Rows are stored
-// unpadded with their 16-byte chunks XOR-swizzled by row, which makes both
-// LDS read patterns conflict-free: the row-wise reads feeding the score
-// product (16 rows, same column chunk) and the transposing reads
-// (ds_read_b64_tr_b16, 4 consecutive rows x 16 columns per lane group)
-// feeding the value product.  Waits on the DMA are explicit vmcnt counts
-// followed by a bare s_barrier; a full workgroup fence would drain every
-// tile in flight.
+// into a three-stage LDS ring with global_load_lds_dwordx4 carrying the
+// non-temporal hint (no register staging).  In LDS a tile is stored as
+// 36 blocks of 1 KiB, [row half (16 rows)][slab of 4 chunks (64 bytes of
+// each row)], one per copy instruction, with the four 16-byte chunks of each
+// row XOR-swizzled by (row % 16) / 4.  Every copy instruction then reads one
+// wave-uniform base plus the same per-lane offset (no per-tile vector
+// address arithmetic), and both LDS read patterns are conflict-free: the
+// row-wise reads feeding the score product (16 rows, one chunk) and the
+// transposing reads (ds_read_b64_tr_b16, 4 consecutive rows x 16 columns per
+// 16-lane group) feeding the value product.  The copies are issued as inline
+// assembly and awaited with explicit vmcnt counts followed by a bare
+// s_barrier; a full workgroup fence, or the compiler's own alias-based
+// waits, would drain every tile in flight.
 //
-// Online softmax in the matrix-core output layout (lane l: head l%16, tokens
-// 4*(l/16)+v of each 16-token half), with lazy rescaling: the running
-// reference max only moves when a tile's max exceeds it by more than 8 (log2
-// units), so the accumulators are rarely rescaled; probabilities stay below
-// 2^8, exact in the fp32 accumulators and representable in bf16.  Both waves
-// of a pair see identical scores, so they take identical softmax decisions.
-#include "cache_addr.h"
+// Online softmax in the matrix-core output layout (lane l: head l%32, tokens
+// 8*(v/4) + 4*(l/32) + v%4 of the tile, v = 0..15), with lazy rescaling: the
+// running reference max only moves when a tile's max exceeds it by more
+// than 8 (log2 units), so the accumulators are rarely rescaled;
+// probabilities stay below 2^8, exact in the fp32 accumulators and
+// representable in bf16.  The value product reduces over tokens in the same
+// per-lane order the scores come out in, so P^T needs no data movement.
 #include "device_common.h"
 #include "kvattn_internal.h"
 
@@ -45,32 +50,41 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kT = 32;                      // tokens per tile
-constexpr int kRowElems = kMlaRow;          // 576 bf16
-constexpr int kRowBytes = kRowElems * 2;    // 1152
-constexpr int kChunks = kRowBytes / 16;     // 72 16-byte chunks per row
-constexpr int kTileBytes = kT * kRowBytes;  // 36864
-constexpr int kNBuf = 3;
-constexpr int kTileInsts = kT * kChunks / 64;  // 36 wave-wide DMA instructions per tile
-constexpr int kKBHalf = kMlaRow / 32 / 2;   // 9 score reduction blocks per wave
-constexpr int kDBHalf = kMlaLatent / 16 / 2;  // 16 output column blocks per wave
-constexpr int kSxBytes = 32 * 1024;         // partial-score exchange: 8 waves x 16 or 4 waves x 32 floats per lane
-constexpr float kRescaleSlack = 8.f;        // log2 units
+constexpr int kT = 32;                         // tokens per tile
+constexpr int kRowElems = kMlaRow;             // 576 bf16
+constexpr int kRowBytes = kRowElems * 2;       // 1152
+constexpr int kChunks = kRowBytes / 16;        // 72 16-byte chunks per row
+constexpr int kTileBytes = kT * kRowBytes;     // 36864
+constexpr int kNBuf = 3;                       // LDS ring stages
+constexpr int kWaves = 8;
+constexpr int kTileInsts = kT * kChunks / 64;  // 36 wave-wide copies per tile
+constexpr int kDmaPer = kTileInsts / kWaves;   // 4 ...
+constexpr int kDmaExtra = kTileInsts % kWaves; // ... plus one for the first 4 waves
+static_assert(kDmaPer == 4 && kDmaExtra == 4, "wait counts in the main loop assume 5 / 4 copies per wave");
+constexpr int kSteps = kMlaRow / 16 / 2;       // 18 score reduction steps per wave
+constexpr int kColBlocks = kMlaLatent / 32 / 2;  // 8 output column blocks per wave
+constexpr int kSxFloats = kWaves * 16 * 64;    // partial-score exchange: 16 floats per lane
+constexpr float kRescaleSlack = 8.f;           // log2 units
+#ifndef MLA_KDEPTH
+#define MLA_KDEPTH 3
+#endif
+#ifndef MLA_VDEPTH
+#define MLA_VDEPTH 3
+#endif
+constexpr int kKDepth = MLA_KDEPTH;            // LDS operand reads in flight, score product
+constexpr int kVDepth = MLA_VDEPTH;            // ... and value product
 
-// Chunk swizzle of row r: XOR of the low three chunk-index bits with a
-// function of the row that makes both read patterns below conflict-free
-// (16 rows x one chunk; 4 consecutive rows x 4 half-chunks).  Rows r and
-// r+16 share it.
-__device__ __forceinline__ int swz(int row) { return (((row >> 1) & 3) << 1) | ((row >> 3) & 1); }
+// LDS byte offset of 16-byte chunk `chunk` (0..71) of tile row `row` (0..31).
+__device__ __forceinline__ int lds_chunk(int row, int chunk) {
+  const int r = row & 15;
+  return (row >> 4) * (kTileBytes / 2) + (chunk >> 2) * 1024 + r * 64 + (((chunk & 3) ^ (r >> 2)) << 4);
+}
 
 // 16-byte global -> LDS copy of every lane: lane i's bytes land at
 // lds_base + 16 * i (lds_base is wave-uniform, taken through M0).  The
-// non-temporal hint marks the cache stream as read-once, which measurably
-// raises the streaming rate on this part.  Issued as
-// inline assembly so the compiler does not treat every later LDS read as a
-// possible alias of the copy and drain all copies in flight; completion is
-// awaited explicitly with vmcnt before the tile is read.  M0 is written here
-// and nowhere else in this kernel.
+// non-temporal hint marks the cache stream as read-once.  Issued as inline
+// assembly so the compiler does not treat every later LDS read as a possible
+// alias of the copy; M0 is written here and nowhere else in this kernel.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
@@ -78,14 +92,27 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory");
 }
 
-// HBW: 16-head blocks per wave.  A pair of waves owns 16*HBW heads, so the
-// workgroup has 2 * 8 / HBW waves for 128 heads (HBW = 4: 4 waves with the
-// full 512-register budget each; HBW = 2: 8 waves, two per SIMD).
-template <int HBW>
-__global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs a) {
-  constexpr int kWaves = 2 * 8 / HBW;
-  constexpr int kDmaPer = kTileInsts / kWaves, kDmaExtra = kTileInsts % kWaves;
-  static_assert(kWaves * HBW * 16 * 4 * 4 <= kSxBytes / 16 * 16, "score exchange must fit");
+// The same copy addressed as a wave-uniform 64-bit base plus a per-lane
+// 32-bit byte offset, so the per-tile address arithmetic is scalar.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+struct TagFalse { static constexpr bool value = false; };
+struct TagTrue { static constexpr bool value = true; };
+
+// Block-table index and in-block slot of token t (paged cache).
+__device__ __forceinline__ int block_of(const DecodeArgs& a, int t) {
+  return a.block_shift >= 0 ? t >> a.block_shift : t / a.block_size;
+}
+__device__ __forceinline__ int slot_of(const DecodeArgs& a, int t) {
+  return a.block_shift >= 0 ? t & (a.block_size - 1) : t % a.block_size;
+}
+
+__global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   // 1-D grid, XCD-aware: workgroup w runs on XCD w % 8, and every split of
   // sequence b gets an id with the same residue, so a sequence's queries and
   // partials stay in one XCD's L2.
@@ -95,8 +122,8 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
   if (b >= a.batch) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave-derived values in SGPRs
-  const int n16 = lane & 15, grp = lane >> 4;
   const int pair = wave >> 1, half = wave & 1;
+  const int c32 = lane & 31, g = lane >> 5;
   const int h = a.num_q_heads;
 
   const int len = clamp_len(a.seq_lens[b], a.len_cap);
@@ -106,258 +133,297 @@ __global__ __launch_bounds__(2 * 8 / HBW * 64, 1) void mla_split_bf16(DecodeArgs
   const int t_end = min(len, t_begin + a.split_tokens);
 
   __shared__ __attribute__((aligned(1024))) unsigned char tiles[kNBuf][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float sx[kSxBytes / 4];
+  __shared__ __attribute__((aligned(16))) float sx[kSxFloats];
 
-  // Q^T fragments of this wave's half of the 576 query dims, for its pair's
-  // 32 heads.  Reduction step kk of lane group grp covers the eight dims of
-  // 16-byte chunk 8*kk + 2*grp + half; the cache rows are read with the same
-  // mapping, so the split between the two waves interleaves chunks.
+  // Q^T fragments of this wave's half of the 576 query dims for its pair's
+  // 32 heads (B operand: lane l holds head l%32).  Step j of lane half g
+  // covers the eight dims of 16-byte chunk 4*j + 2*half + g; the cache rows
+  // are read with the same mapping.  Heads past h (h a multiple of 16) are
+  // computed on a copy of the last head and never stored: branching around
+  // the matrix work would cost more registers than it saves.
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (int64_t)b * h * kRowElems;
-  bf16x8 qf[HBW][kKBHalf];
+  bf16x8 qf[kSteps];
+  {
+    const int head = min(32 * pair + c32, h - 1);
 #pragma unroll
-  for (int hbi = 0; hbi < HBW; ++hbi) {
-    const int head = (HBW * pair + hbi) * 16 + n16;
-#pragma unroll
-    for (int kk = 0; kk < kKBHalf; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if ((HBW * pair + hbi) * 16 < h)  // h is a multiple of 16: whole head blocks are in or out
-        v = *reinterpret_cast<const u32x4*>(qb + (int64_t)head * kRowElems + 8 * (8 * kk + 2 * grp + half));
-      qf[hbi][kk] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int j = 0; j < kSteps; ++j)
+      qf[j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(qb + (int64_t)head * kRowElems + 8 * (4 * j + 2 * half + g)));
   }
-
   // Let the query loads land now: the compiler cannot see the tile copies in
   // the vector-memory counter, and any wait it places on these loads inside
   // the loop would also drain the copies in flight.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  f32x4 acc[HBW][kDBHalf];
-  float m_ref[HBW], l_run[HBW];
+  f32x16 acc[kColBlocks];
 #pragma unroll
-  for (int hbi = 0; hbi < HBW; ++hbi) {
-    m_ref[hbi] = -INFINITY;
-    l_run[hbi] = 0.f;
+  for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
-    for (int db = 0; db < kDBHalf; ++db) acc[hbi][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
   const uint16_t* cbase = static_cast<const uint16_t*>(a.k);
-  // DMA of one tile: 36 wave instructions spread over the waves (the first
-  // kDmaExtra waves take one more).  Instruction `inst` fills LDS chunks
-  // [inst*64, +64) of the tile; lane l's chunk L sits in row L / 72 at
-  // physical slot L % 72 and holds logical chunk (slot ^ swz(row)).
+  // Copies of one tile: 36 wave instructions spread over the waves (the
+  // first kDmaExtra waves take one more).  Instruction `inst` fills LDS
+  // block inst: rows 16*(inst/18) + (lane/4) of the tile, slab inst%18, and
+  // lane l lands at physical chunk l%4 of its row's slab, which holds
+  // logical chunk 4*slab + ((l%4) ^ (l/16)).
   const int inst0 = wave * kDmaPer + min(wave, kDmaExtra);
   const int ninst = kDmaPer + (wave < kDmaExtra ? 1 : 0);
+  const int drow = lane >> 2, dchunk = (lane & 3) ^ (lane >> 4);
+  // Byte offset of the lane's source inside a 16-row run of cache rows (slab 0).
+  const uint32_t doff = (uint32_t)((drow * kRowElems + dchunk * 8) * 2);
   // Contiguous rows of this sequence start here; a paged cache looks each row up.
   const uint16_t* seq_base = cbase + (a.block_size == 0 ? (int64_t)b * a.cache_len * kRowElems : 0);
-  auto issue_tile = [&](int t0, int buf) {
+  const int32_t* tbl = a.block_table + (int64_t)b * a.max_blocks;
+  // Fast copies need each 16-row half of the tile to be one run of
+  // consecutive cache rows: always true for a contiguous cache, and for a
+  // paged one whose block size is a multiple of 16 (tiles start at
+  // multiples of 32 tokens).  The ragged last tile of a split takes the
+  // general path, which clamps every row into the split.
+  const bool halves_contiguous = a.block_size == 0 || (a.block_size & 15) == 0;
+  auto issue_tile = [&](int t0, int buf) __attribute__((always_inline)) {
     const uint32_t dst = (uint32_t)(uintptr_t)&tiles[buf][0];
-    // An opaque copy of the lane id: the per-lane DMA offsets are recomputed
-    // here (a few integer ops) instead of being kept live across the loop.
-    int ln;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
-    if (a.block_size == 0) {
+    if (halves_contiguous && t0 + kT <= t_end) {
+      const uint16_t* base[2];
+      if (a.block_size == 0) {
+        base[0] = seq_base + (int64_t)t0 * kRowElems;
+        base[1] = base[0] + 16 * kRowElems;
+      } else {
+        // Scalar table loads (counted by lgkmcnt) leave the copies in flight alone.
+        const int32_t* ep0 = tbl + block_of(a, t0);
+        const int32_t* ep1 = tbl + block_of(a, t0 + 16);
+        int e0, e1;
+        asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&s"(e0), "=&s"(e1)
+                     : "s"(ep0), "s"(ep1)
+                     : "memory");
+        // An out-of-range table entry reads the pool's first rows instead.
+        base[0] = (e0 < 0 || (int64_t)e0 >= a.cache_len)
+                      ? cbase
+                      : cbase + ((int64_t)e0 * a.block_size + slot_of(a, t0)) * kRowElems;
+        base[1] = (e1 < 0 || (int64_t)e1 >= a.cache_len)
+                      ? cbase
+                      : cbase + ((int64_t)e1 * a.block_size + slot_of(a, t0 + 16)) * kRowElems;
+      }
 #pragma unroll
-      for (int u = 0; u < kDmaPer + (kDmaExtra ? 1 : 0); ++u) {
+      for (int u = 0; u < kDmaPer + 1; ++u) {
         if (u < ninst) {
           const int inst = inst0 + u;
-          const int L = inst * 64 + ln;
-          const int row = L / kChunks;
-          const int chunk = (L - row * kChunks) ^ swz(row);
-          const int t = min(t0 + row, t_end - 1);  // rows past the end re-read the last valid row (masked below)
-          dma16(seq_base + (int64_t)t * kRowElems + chunk * 8, dst + inst * 1024);
+          const int slab = inst % 18;
+          dma16s(doff, base[inst / 18] + slab * 32, dst + inst * 1024);
         }
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kDmaPer + (kDmaExtra ? 1 : 0); ++u) {
-        if (u < ninst) {
-          const int inst = inst0 + u;
-          const int L = inst * 64 + ln;
-          const int row = L / kChunks;
-          const int chunk = (L - row * kChunks) ^ swz(row);
-          const int t = min(t0 + row, t_end - 1);
-          int64_t off = cache_row_offset(a, b, 0, t, kRowElems);
-          off = off < 0 ? 0 : off;  // an out-of-range table entry reads row 0 of the pool instead
-          dma16(cbase + off + chunk * 8, dst + inst * 1024);
+      return;
+    }
+    // General path: per-lane row addresses, rows past the end clamped to the
+    // last valid row (their scores are masked).  Not unrolled: it is rare,
+    // and the loop keeps its temporaries out of the registers the main loop
+    // needs.
+#pragma unroll 1
+    for (int u = 0; u < kDmaPer + 1; ++u) {
+      if (u < ninst) {
+        const int inst = inst0 + u;
+        const int t = min(t0 + 16 * (inst / 18) + drow, t_end - 1);
+        const int chunk = 4 * (inst % 18) + dchunk;
+        int64_t off;
+        if (a.block_size == 0) {
+          off = (int64_t)t * kRowElems;
+        } else {
+          const int blk = tbl[block_of(a, t)];
+          // An out-of-range table entry reads row 0 of the pool instead.
+          off = (blk < 0 || (int64_t)blk >= a.cache_len) ? -(int64_t)(seq_base - cbase)
+                                                          : ((int64_t)blk * a.block_size + slot_of(a, t)) * kRowElems;
         }
+        dma16(seq_base + off + chunk * 8, dst + inst * 1024);
       }
     }
   };
+
+  // Per-lane LDS byte offsets inside a tile.
+  // Scores (A operand): lane l reads row l%32 at chunk 4*j + 2*half + l/32,
+  // i.e. the per-lane offset below plus an immediate 1024 * j.
+  const int koff = lds_chunk(c32, 2 * half + g);
+  // Values (A operand): lane l needs column 32*cb + l%32 at the tokens of
+  // step kk, two runs of four rows.  The transposing read returns to lane n
+  // of a 16-lane group element n%4 of the 4-element piece addressed by lane
+  // 4v + n/4, for rows v = 0..3; so lane n of group G addresses row
+  // 4*(G/2) + n/4 (+8 for the second run, +16*kk) and the four columns
+  // 32*cb + 16*(G%2) + 4*(n%4) .. +3 (chunk 4*cb + 2*(G%2) + (n%4)/2, byte
+  // 8*(n%2)), and receives column 32*cb + 16*(G%2) + n.  Column block
+  // cb = 2*i + half adds an immediate 2048 * i, step kk one of 16 rows.
+  const int vn = lane & 15, vgrp = lane >> 4;
+  const int vchunk = 4 * half + 2 * (vgrp & 1) + ((vn & 3) >> 1);
+  const int vrow0 = 4 * (vgrp >> 1) + (vn >> 2);
+  const int voff0 = lds_chunk(vrow0, vchunk) + 8 * (vn & 1);
+  const int voff1 = lds_chunk(vrow0 + 8, vchunk) + 8 * (vn & 1);
 
   const int ntok = t_end - t_begin;
   const int n_tiles = ntok > 0 ? (ntok + kT - 1) / kT : 0;
   if (n_tiles > 0) issue_tile(t_begin, 0);
   if (n_tiles > 1) issue_tile(t_begin + kT, 1);
 
-
-  for (int it = 0; it < n_tiles; ++it) {
-    // Wait for this tile's DMA (the next tile's may stay in flight), then sync.
-    if (it + 1 < n_tiles) {
-      if constexpr (kWaves == 8) {
-        static_assert(kDmaPer == 4 && kDmaExtra == 4, "wait counts below");
-        if (wave < 4) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      } else {
-        static_assert(kWaves == 4 && kDmaPer == 9 && kDmaExtra == 0, "wait counts below");
-        asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
+  // One tile: wait for its copies, issue the copies of tile it+2, scores,
+  // partial-score swap, softmax, value product.  kLast marks the last tile
+  // of the split, the only one that can be ragged; the others are compiled
+  // without any masking.
+  auto tile_step = [&](int it, auto last_tag) __attribute__((always_inline)) {
+    constexpr bool kLast = decltype(last_tag)::value;
+    // Wait for this tile's copies (the next tile's may stay in flight), then
+    // sync; afterwards tile it+2 may go into the stage tile it-1 used.
+    if constexpr (!kLast) {
+      if (wave < kDmaExtra) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (it + 2 < n_tiles) issue_tile(t_begin + (it + 2) * kT, (it + 2) % kNBuf);
     } else {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (it + 2 < n_tiles) issue_tile(t_begin + (it + 2) * kT, (it + 2) % kNBuf);
     const int t0 = t_begin + it * kT;
     const unsigned char* tile = tiles[it % kNBuf];
     const auto* tile_lds = (const __attribute__((address_space(3))) unsigned char*)tile;
-    // Per-lane LDS byte offsets inside a tile (see the read lambdas below),
-    // recomputed per tile from an opaque lane id to keep them out of the
-    // registers that live across the loop.
-    int ln;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
-    const int ln16 = ln & 15, lgrp = ln >> 4;
-    const int koff = ln16 * kRowBytes + 16 * ((2 * lgrp + half) ^ swz(ln16));
 
-    // Partial scores over this wave's half of the 576 dims.
-    f32x4 s[2][HBW];
+    // Partial scores over this wave's half of the dims.
+    f32x16 s;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int hbi = 0; hbi < HBW; ++hbi) s[st][hbi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // One k-block of operands is read ahead of the matrix ops that use the
-    // previous one; the scheduling barriers keep the compiler from hoisting
-    // every read.  The swizzle only touches per-lane chunk bits, so the
-    // step kk and the half st are immediate offsets.
-    auto read_k = [&](int kk, int st) {
-      return __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(tile + koff + st * 16 * kRowBytes + 128 * kk));
+    for (int v = 0; v < 16; ++v) s[v] = 0.f;
+    auto read_k = [&](int j) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + koff + 1024 * j));
     };
-    bf16x8 ka_next[2] = {read_k(0, 0), read_k(0, 1)};
+    bf16x8 ka[kKDepth];
 #pragma unroll
-    for (int kk = 0; kk < kKBHalf; ++kk) {
-      const bf16x8 ka[2] = {ka_next[0], ka_next[1]};
-      if (kk + 1 < kKBHalf) {
-        ka_next[0] = read_k(kk + 1, 0);
-        ka_next[1] = read_k(kk + 1, 1);
-      }
+    for (int j = 0; j + 1 < kKDepth; ++j) ka[j] = read_k(j);
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int hbi = 0; hbi < HBW; ++hbi)
-          s[st][hbi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[st], qf[hbi][kk], s[st][hbi], 0, 0, 0);
+    for (int j = 0; j < kSteps; ++j) {
+      if (j + kKDepth - 1 < kSteps) ka[(j + kKDepth - 1) % kKDepth] = read_k(j + kKDepth - 1);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j % kKDepth], qf[j], s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Swap partial scores with the other wave of the pair.
-    // Each lane stores its four-score fragments as 16-byte words, consecutive
-    // across lanes.
-    f32x4* mine = reinterpret_cast<f32x4*>(sx) + wave * (2 * HBW) * 64;
-    const f32x4* other = reinterpret_cast<const f32x4*>(sx) + (wave ^ 1) * (2 * HBW) * 64;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int hbi = 0; hbi < HBW; ++hbi) mine[(st * HBW + hbi) * 64 + lane] = s[st][hbi];
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int hbi = 0; hbi < HBW; ++hbi) {
-        // Add in a fixed order (lower half first) so both waves get identical sums.
-        const f32x4 o = other[(st * HBW + hbi) * 64 + lane];
-        s[st][hbi] = half == 0 ? s[st][hbi] + o : o + s[st][hbi];
-      }
 
-    // Online softmax; P^T packed straight into the B-operand layout.  Only the
-    // last tile of a split can hold tokens past its end.
-    const bool ragged = t0 + kT > t_end;
-    bf16x8 pp[HBW];
+    // Swap partial scores with the other wave of the pair: each lane stores
+    // its 16 scores as four 16-byte words, consecutive across lanes.
+    f32x4* mine = reinterpret_cast<f32x4*>(sx) + wave * 4 * 64;
+    const f32x4* other = reinterpret_cast<const f32x4*>(sx) + (wave ^ 1) * 4 * 64;
 #pragma unroll
-    for (int hbi = 0; hbi < HBW; ++hbi) {
-      float sv[8];
+    for (int q = 0; q < 4; ++q) mine[q * 64 + lane] = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float sv[16];  // raw scores q.k
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+    for (int q = 0; q < 4; ++q) {
+      // Add in a fixed order (lower half first) so both waves get identical sums.
+      const f32x4 o = other[q * 64 + lane];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) sv[4 * st + v] = s[st][hbi][v] * a.scale_log2;
-      if (ragged) {
+      for (int e = 0; e < 4; ++e) sv[4 * q + e] = half == 0 ? s[4 * q + e] + o[e] : o[e] + s[4 * q + e];
+    }
+
+    // Online softmax on c * score (c = scale * log2 e, log2 units); P^T is
+    // packed straight into the B-operand layout.  The tile maximum of c * s
+    // is c times the raw maximum (the minimum, for a negative scale).  Only
+    // the last tile of a split can hold tokens past its end; its masked
+    // scores are set to the neutral element of that extremum and their
+    // probabilities to zero.
+    const float c = a.scale_log2;
+    const float neutral = c >= 0.f ? -INFINITY : INFINITY;
+    if constexpr (kLast) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (t0 + 16 * (e >> 2) + 4 * grp + (e & 3) >= t_end) sv[e] = -INFINITY;
-      }
-      float mt = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mt = max_over_row_groups(mt);
-      const bool need = mt > m_ref[hbi] + kRescaleSlack;  // also true while m_ref is -inf
-      if (__any(need)) {
-        const float m_new = need ? mt : m_ref[hbi];
-        const float alpha = fast_exp2(m_ref[hbi] - m_new);
-        m_ref[hbi] = m_new;
-        l_run[hbi] *= alpha;
+      for (int v = 0; v < 16; ++v)
+        if (t0 + 8 * (v >> 2) + 4 * g + (v & 3) >= t_end) sv[v] = neutral;
+    }
+    float ext;
+    if (c >= 0.f) {
+      ext = sv[0];
 #pragma unroll
-        for (int db = 0; db < kDBHalf; ++db) acc[hbi][db] *= alpha;
-      }
+      for (int v = 1; v < 16; ++v) ext = fmaxf(ext, sv[v]);
+    } else {
+      ext = sv[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) ext = fminf(ext, sv[v]);
+    }
+    const float mt = max_over_halves(ext * c);
+    const bool need = mt > m_ref + kRescaleSlack;  // also true while m_ref is -inf
+    if (__any(need)) {
+      const float m_new = need ? mt : m_ref;
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < kColBlocks; ++i) acc[i] *= alpha;
+    }
+    float pv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) pv[v] = fast_exp2(__builtin_fmaf(sv[v], c, -m_ref));
+    if constexpr (kLast) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (t0 + 8 * (v >> 2) + 4 * g + (v & 3) >= t_end) pv[v] = 0.f;
+    }
+    // Reduction step kk of the value product takes the lane's scores
+    // v = 8*kk .. 8*kk+7, i.e. tokens 16*kk + 8*(e/4) + 4*(l/32) + e%4.
+    bf16x8 pp[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
       u32x4 packed;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        packed[e] = pack_bf16x2(fast_exp2(sv[2 * e] - m_ref[hbi]), fast_exp2(sv[2 * e + 1] - m_ref[hbi]));
-        l_run[hbi] = add_bf16x2(packed[e], l_run[hbi]);  // normalise with the weights the matrix core sees
+        packed[e] = pack_bf16x2(pv[8 * kk + 2 * e], pv[8 * kk + 2 * e + 1]);
+        l_run = add_bf16x2(packed[e], l_run);  // normalise with the weights the matrix core sees
       }
-      pp[hbi] = __builtin_bit_cast(bf16x8, packed);
+      pp[kk] = __builtin_bit_cast(bf16x8, packed);
     }
 
-    // Values: O^T[16 cols x 16 heads] += V^T[16 cols x 32 tokens] * P^T for
-    // this wave's 256 latent columns.  The transposing read returns to lane n
-    // of a 16-lane group element n%4 of the 4-element piece addressed by lane
-    // 4v + n/4, for rows v = 0..3; lane L = 4v + c addresses token row
-    // 4*grp + v (and +16) and piece c of the column block, so lane n receives
-    // column start(db) + n.  Column block db covers latent columns
-    // 64*(db/2) + 32*half + 16*(db%2) .. +15.
-    const int vrow = 4 * lgrp + (ln16 >> 2);
-    const int vc = ln16 & 3;
-    const int voff_even = vrow * kRowBytes + 16 * ((4 * half + (vc >> 1)) ^ swz(vrow)) + 8 * (vc & 1);
-    const int voff_odd = vrow * kRowBytes + 16 * ((4 * half + 2 + (vc >> 1)) ^ swz(vrow)) + 8 * (vc & 1);
-    auto read_v = [&](int db) {
-      const int off = ((db & 1) ? voff_odd : voff_even) + 128 * (db >> 1);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_lds + off));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_lds + off + 16 * kRowBytes));
+    // Values: O^T[32 cols x 32 heads] += V^T[32 cols x 16 tokens] * P^T per
+    // step kk, for this wave's column blocks cb = 2*i + half (latent columns
+    // 32*cb .. 32*cb+31).  Steps run kk-major, so consecutive matrix ops
+    // accumulate into different blocks.
+    auto read_v = [&](int i, int kk) __attribute__((always_inline)) {
+      const int imm = 2048 * i + (kTileBytes / 2) * kk;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_lds + voff0 + imm));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_lds + voff1 + imm));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8 va_next = read_v(0);
+    constexpr int kVSteps = 2 * kColBlocks;
+    bf16x8 va[kVDepth];
 #pragma unroll
-    for (int db = 0; db < kDBHalf; ++db) {
-      const bf16x8 va = va_next;
-      if (db + 1 < kDBHalf) va_next = read_v(db + 1);
+    for (int st = 0; st + 1 < kVDepth; ++st) va[st] = read_v(st % kColBlocks, st / kColBlocks);
 #pragma unroll
-      for (int hbi = 0; hbi < HBW; ++hbi)
-        acc[hbi][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pp[hbi], acc[hbi][db], 0, 0, 0);
+    for (int st = 0; st < kVSteps; ++st) {
+      const int nx = st + kVDepth - 1;
+      if (nx < kVSteps) va[nx % kVDepth] = read_v(nx % kColBlocks, nx / kColBlocks);
+      const int i = st % kColBlocks, kk = st / kColBlocks;
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[st % kVDepth], pp[kk], acc[i], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  for (int it = 0; it + 1 < n_tiles; ++it) tile_step(it, TagFalse{});
+  if (n_tiles > 0) tile_step(n_tiles - 1, TagTrue{});
 
-  // Lane l holds O^T[col = start(db) + 4*grp + v][head (HBW*pair+hbi)*16 + n16].
+  // Lane l holds O^T[col = 32*cb + 8*(v/4) + 4*(l/32) + v%4][head 32*pair + l%32].
+  const int head = 32 * pair + c32;
+  if (head >= h) return;
+  const float l = sum_over_halves(l_run);
+  const int64_t row = (int64_t)b * h + head;
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  const float lse2 = empty ? -INFINITY : m_ref + __log2f(l);
+  if (final_out) {
+    uint16_t* o = static_cast<uint16_t*>(a.out) + row * kMlaLatent + 4 * g;
 #pragma unroll
-  for (int hbi = 0; hbi < HBW; ++hbi) {
-    const int head = (HBW * pair + hbi) * 16 + n16;
-    if (head >= h) continue;
-    const float l = sum_over_row_groups(l_run[hbi]);
-    const int64_t row = (int64_t)b * h + head;
-    const bool empty = !(l > 0.f);
-    const float inv = empty ? 0.f : 1.f / l;
-    const float lse2 = empty ? -INFINITY : m_ref[hbi] + __log2f(l);
-    const int col0 = 32 * half + 4 * grp;
-    if (final_out) {
-      uint16_t* o = static_cast<uint16_t*>(a.out) + row * kMlaLatent + col0;
+    for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
-      for (int db = 0; db < kDBHalf; ++db) {
-        const int start = 64 * (db >> 1) + 16 * (db & 1);
-        const uint32_t lo = pack_bf16x2(acc[hbi][db][0] * inv, acc[hbi][db][1] * inv);
-        const uint32_t hi = pack_bf16x2(acc[hbi][db][2] * inv, acc[hbi][db][3] * inv);
-        *reinterpret_cast<uint2*>(o + start) = make_uint2(lo, hi);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = pack_bf16x2(acc[i][4 * q] * inv, acc[i][4 * q + 1] * inv);
+        const uint32_t hi = pack_bf16x2(acc[i][4 * q + 2] * inv, acc[i][4 * q + 3] * inv);
+        *reinterpret_cast<uint2*>(o + 32 * (2 * i + half) + 8 * q) = make_uint2(lo, hi);
       }
-      if (a.lse != nullptr && grp == 0 && half == 0) a.lse[row] = lse2 * kLn2;
-    } else {
-      float* po = a.part_o + (row * a.n_split + split) * kMlaLatent + col0;
+    if (a.lse != nullptr && g == 0 && half == 0) a.lse[row] = lse2 * kLn2;
+  } else {
+    float* po = a.part_o + (row * a.n_split + split) * kMlaLatent + 4 * g;
 #pragma unroll
-      for (int db = 0; db < kDBHalf; ++db)
-        *reinterpret_cast<f32x4*>(po + 64 * (db >> 1) + 16 * (db & 1)) = acc[hbi][db] * inv;
-      if (grp == 0 && half == 0) a.part_lse[row * a.n_split + split] = lse2;
-    }
+    for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(po + 32 * (2 * i + half) + 8 * q) =
+            f32x4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]} * inv;
+    if (g == 0 && half == 0) a.part_lse[row * a.n_split + split] = lse2;
   }
 }
 
@@ -367,7 +433,7 @@ hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_q_heads % 16 != 0 || a.num_q_heads > kMaxMlaHeads) return hipErrorInvalidValue;
   const int seq_groups = (a.batch + 7) / 8;
   const dim3 grid(8 * seq_groups * a.n_split);
-  mla_split_bf16<2><<<grid, dim3(512), 0, stream>>>(a);
+  mla_split_bf16<<<grid, dim3(kWaves * 64), 0, stream>>>(a);
   return hipGetLastError();
 }
 
