@@ -25,4 +25,5 @@ from .kvattn import (  # noqa: F401
     load_library,
     mla_decode,
     mla_workspace_bytes,
+    time_next_kernel,
 )

@@ -16,6 +16,14 @@
 namespace {
 
 thread_local std::string g_last_error;
+// Events the next decode call on this thread records around its split-K kernel.
+thread_local kvattn::LaunchEvents g_time_next;
+
+kvattn::LaunchEvents take_timing_events() {
+  const kvattn::LaunchEvents ev = g_time_next;
+  g_time_next = kvattn::LaunchEvents{};
+  return ev;
+}
 
 kvattn_status fail(kvattn_status s, const char* fmt, long long a = 0, long long b = 0) {
   char buf[256];
@@ -213,6 +221,7 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
                                 int32_t num_kv_heads, int32_t head_dim, int64_t cache_len, int32_t block_size,
                                 int32_t max_blocks_per_seq, int32_t max_seq_len, float scale, kvattn_dtype dtype,
                                 int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  const kvattn::LaunchEvents ev = take_timing_events();  // armed for this call only, whatever its outcome
   kvattn_status st = check_gqa(q, k_cache, v_cache, seq_lens, out, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                                scale);
   if (st != KVATTN_OK) return st;
@@ -254,7 +263,7 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
     a.part_lse = a.part_o + (int64_t)batch * num_q_heads * nsplit * head_dim;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == KVATTN_BF16 ? kvattn::launch_gqa_bf16(a, s) : kvattn::launch_gqa_f32(a, s);
+  hipError_t e = dtype == KVATTN_BF16 ? kvattn::launch_gqa_bf16(a, s, ev) : kvattn::launch_gqa_f32(a, s, ev);
   if (e != hipSuccess) return hip_status(e, "split kernel launch");
   if (nsplit > 1) {
     e = kvattn::launch_merge(a, head_dim, dtype == KVATTN_BF16, s);
@@ -268,6 +277,7 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
                                 int32_t d_rope, int64_t cache_len, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t max_seq_len, float scale, kvattn_dtype dtype, int32_t split_tokens,
                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const kvattn::LaunchEvents ev = take_timing_events();  // armed for this call only, whatever its outcome
   kvattn_status st = check_mla(q, cache, seq_lens, out, batch, num_heads, d_latent, d_rope, dtype, scale);
   if (st != KVATTN_OK) return st;
   const bool paged = block_table != nullptr;
@@ -307,12 +317,20 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
     a.part_lse = a.part_o + (int64_t)batch * num_heads * nsplit * d_latent;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = kvattn::launch_mla_bf16(a, s);
+  hipError_t e = kvattn::launch_mla_bf16(a, s, ev);
   if (e != hipSuccess) return hip_status(e, "MLA kernel launch");
   if (nsplit > 1) {
     e = kvattn::launch_merge(a, d_latent, true, s);
     if (e != hipSuccess) return hip_status(e, "merge kernel launch");
   }
+  return ok();
+}
+
+kvattn_status kvattn_time_next_kernel(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(KVATTN_ERR_INVALID, "start_event and stop_event must both be set or both be null");
+  g_time_next.start = static_cast<hipEvent_t>(start_event);
+  g_time_next.stop = static_cast<hipEvent_t>(stop_event);
   return ok();
 }
 

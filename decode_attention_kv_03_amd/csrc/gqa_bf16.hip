@@ -345,19 +345,19 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
 }
 
 template <int NST>
-hipError_t launch_depth(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_depth(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
   const int64_t units = (int64_t)a.batch * a.num_kv_heads;
   const dim3 grid((unsigned)(8 * ((units + 7) / 8) * a.n_split));
   const dim3 block(256);
   const int head_blocks = (a.group + 15) / 16;
   if (head_blocks == 1) {
-    gqa_split_bf16<1, 4, NST><<<grid, block, 0, stream>>>(a);
+    hipExtLaunchKernelGGL((gqa_split_bf16<1, 4, NST>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
   } else if (head_blocks == 2) {
-    gqa_split_bf16<1, 2, NST><<<grid, block, 0, stream>>>(a);
+    hipExtLaunchKernelGGL((gqa_split_bf16<1, 2, NST>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
   } else if (head_blocks <= 4) {
-    gqa_split_bf16<1, 1, NST><<<grid, block, 0, stream>>>(a);
+    hipExtLaunchKernelGGL((gqa_split_bf16<1, 1, NST>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
   } else if (head_blocks <= 8) {
-    gqa_split_bf16<2, 1, NST><<<grid, block, 0, stream>>>(a);
+    hipExtLaunchKernelGGL((gqa_split_bf16<2, 1, NST>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -366,8 +366,8 @@ hipError_t launch_depth(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream) {
-  return a.ring_depth == 3 ? launch_depth<3>(a, stream) : launch_depth<2>(a, stream);
+hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
+  return a.ring_depth == 3 ? launch_depth<3>(a, stream, ev) : launch_depth<2>(a, stream, ev);
 }
 
 }  // namespace kvattn

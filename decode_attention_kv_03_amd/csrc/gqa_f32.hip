@@ -159,10 +159,10 @@ __global__ __launch_bounds__(256) void gqa_split_f32(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
   if (a.group > kMaxGroupF32) return hipErrorInvalidValue;
   const dim3 grid(a.n_split, a.num_kv_heads, a.batch);
-  gqa_split_f32<<<grid, dim3(256), 0, stream>>>(a);
+  hipExtLaunchKernelGGL(gqa_split_f32, grid, dim3(256), 0, stream, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // Host <-> kernel interface of libkvattn (not part of the public C ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -46,9 +47,15 @@ struct DecodeArgs {
   int32_t ring_depth;       // bf16 GQA: LDS ring stages (2 or 3)
 };
 
-hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream);
+// Optional events recorded when a launch's kernel starts and ends (null: none).
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
+hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
+hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_hbm_read_probe(const void* buf, int64_t n16, uint32_t* sink, int workgroups, hipStream_t stream);
 // Log-sum-exp merge of the per-split partials into out/lse; d_v = 128 or 512.
 hipError_t launch_merge(const DecodeArgs& a, int d_v, bool out_bf16, hipStream_t stream);

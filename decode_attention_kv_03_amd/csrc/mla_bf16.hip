@@ -429,11 +429,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
   if (a.num_q_heads % 16 != 0 || a.num_q_heads > kMaxMlaHeads) return hipErrorInvalidValue;
   const int seq_groups = (a.batch + 7) / 8;
   const dim3 grid(8 * seq_groups * a.n_split);
-  mla_split_bf16<<<grid, dim3(kWaves * 64), 0, stream>>>(a);
+  hipExtLaunchKernelGGL(mla_split_bf16, grid, dim3(kWaves * 64), 0, stream, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 

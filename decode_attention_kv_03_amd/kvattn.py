@@ -36,6 +36,7 @@ SIGNATURES = {
     "kvattn_mla_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_gqa_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_mla_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "kvattn_time_next_kernel": (_c_i32, [_c_vp, _c_vp]),
     "kvattn_hbm_read_probe": (_c_i32, [_c_vp, _c_sz, _c_vp, _c_i32, _c_vp]),
     "kvattn_status_string": (ctypes.c_char_p, [_c_i32]),
     "kvattn_last_error": (ctypes.c_char_p, []),
@@ -118,6 +119,22 @@ def hbm_read_probe(buf, workgroups, sink, stream=None):
     lib = load_library()
     _check(lib.kvattn_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(workgroups),
                                      _stream(stream)))
+
+
+def time_next_kernel(start_event, stop_event):
+    """Arm two timing-enabled events (torch.cuda.Event) around the split-K kernel of this thread's next
+    decode call (measurement utility; see kvattn_time_next_kernel).  None, None disarms."""
+    lib = load_library()
+    if start_event is None and stop_event is None:
+        _check(lib.kvattn_time_next_kernel(None, None))
+        return
+    handles = []
+    for ev in (start_event, stop_event):
+        h = ev.cuda_event
+        if not h:
+            raise ValueError("time_next_kernel: record each event once first so that it exists")
+        handles.append(ctypes.c_void_p(h))
+    _check(lib.kvattn_time_next_kernel(*handles))
 
 
 def gqa_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0, split_tokens=0,

@@ -1,0 +1,141 @@
+"""Turn rocprofv3 output into the short text summaries kept under profiles/.
+
+    python -m decode_attention_kv_03_amd.profiling trace STATS_CSV OUT_MD TITLE COMMAND
+    python -m decode_attention_kv_03_amd.profiling traffic WORKLOAD OUT_MD FETCH_DIR WRITE_DIR \
+        COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES COMMANDS
+
+``trace`` condenses a ``--kernel-trace --stats`` kernel_stats.csv into a table
+of the library's kernels.  ``traffic`` turns two ``--pmc`` runs of a workload
+(FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) into HBM bytes per launch of
+the split-K kernel, each scaled by what the same counter reads for a plain
+device copy of known size, and records the hash of the kernel sources the
+counters were taken with.  ``bench.py`` reports that traffic only while the
+sources still hash the same.
+"""
+
+import csv
+import glob
+import hashlib
+import os
+import re
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(os.path.dirname(_HERE), "profiles")
+_TAG = re.compile(r"<!-- kvattn-traffic (.*?) -->")
+
+
+def source_sha():
+    """sha256 over the library's kernel and dispatch sources (file names and contents)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(_HERE, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_rows(run_dir):
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _mean_counter(run_dir, counter, match):
+    vals = [float(r["Counter_Value"]) for r in _counter_rows(run_dir)
+            if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+    if not vals:
+        raise ValueError(f"{counter}: no dispatch matched in {run_dir}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _is_split(name):
+    return "kvattn" in name and "split" in name
+
+
+def _is_copy(name):
+    return "kvattn" not in name and ("copy" in name.lower() or "elementwise" in name.lower())
+
+
+def summarize_trace(stats_csv, out_md, title, command):
+    with open(stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    keep = [r for r in rows if "kvattn" in r["Name"]]
+    with open(out_md, "w") as f:
+        f.write(f"# {title}\n\n")
+        f.write("Command (from the repository root, on one MI355X; rocprofv3 --stats output, kernel_stats.csv):\n\n")
+        f.write("```\n" + command + "\n```\n\n")
+        f.write("| kernel | calls | avg (us) | min (us) | max (us) | stddev (us) |\n|---|---|---|---|---|---|\n")
+        for r in keep:
+            f.write(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                    f"{float(r['StdDev']) / 1e3:.2f} |\n")
+        other = len(rows) - len(keep)
+        f.write(f"\nOther kernels in the trace ({other}) are input generation and copies outside the timed region.\n")
+        f.write(f"\nKernel sources hash: `{source_sha()}`\n")
+
+
+def summarize_traffic(workload, out_md, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, commands):
+    fetch_kib, n_f = _mean_counter(fetch_dir, "FETCH_SIZE", _is_split)
+    write_kib, n_w = _mean_counter(write_dir, "WRITE_SIZE", _is_split)
+    cfetch_kib, _ = _mean_counter(copy_fetch_dir, "FETCH_SIZE", _is_copy)
+    cwrite_kib, _ = _mean_counter(copy_write_dir, "WRITE_SIZE", _is_copy)
+    fetch_scale = copy_bytes / (cfetch_kib * 1024.0)
+    write_scale = copy_bytes / (cwrite_kib * 1024.0)
+    fetch_b = fetch_kib * 1024.0 * fetch_scale
+    write_b = write_kib * 1024.0 * write_scale
+    sha = source_sha()
+    with open(out_md, "w") as f:
+        f.write(f"# HBM traffic of the split-K kernel: {workload}\n\n")
+        f.write("rocprofv3 counter runs (one counter per pass), from the repository root on one MI355X:\n\n")
+        f.write("```\n" + commands + "\n```\n\n")
+        f.write("| quantity | value |\n|---|---|\n")
+        f.write(f"| FETCH_SIZE per dispatch, split-K kernel (KiB, mean of {n_f}) | {fetch_kib:.1f} |\n")
+        f.write(f"| WRITE_SIZE per dispatch, split-K kernel (KiB, mean of {n_w}) | {write_kib:.1f} |\n")
+        f.write(f"| FETCH_SIZE of a {copy_bytes} B device copy (KiB) | {cfetch_kib:.1f} |\n")
+        f.write(f"| WRITE_SIZE of the same copy (KiB) | {cwrite_kib:.1f} |\n")
+        f.write(f"| fetch scale (true bytes per counted byte) | {fetch_scale:.4f} |\n")
+        f.write(f"| write scale | {write_scale:.4f} |\n")
+        f.write(f"| HBM bytes read per launch (scaled) | {fetch_b:.0f} |\n")
+        f.write(f"| HBM bytes written per launch (scaled) | {write_b:.0f} |\n")
+        f.write(f"| total traffic per launch | {fetch_b + write_b:.0f} |\n\n")
+        f.write(f"Kernel sources hash: `{sha}`\n\n")
+        f.write(f"<!-- kvattn-traffic workload={workload} source_sha={sha} fetch_bytes={fetch_b:.0f} "
+                f"write_bytes={write_b:.0f} -->\n")
+
+
+def lookup_traffic(workload):
+    """Traffic per split-K launch recorded for `workload` with the current sources, or None."""
+    sha = source_sha()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as fh:
+            for m in _TAG.finditer(fh.read()):
+                kv = dict(item.split("=", 1) for item in m.group(1).split())
+                if kv.get("workload") == workload and kv.get("source_sha") == sha:
+                    return {"fetch_bytes": int(kv["fetch_bytes"]), "write_bytes": int(kv["write_bytes"]),
+                            "source": os.path.relpath(path, os.path.dirname(PROFILES))}
+    return None
+
+
+def main(argv):
+    if len(argv) >= 5 and argv[0] == "trace":
+        summarize_trace(argv[1], argv[2], argv[3], argv[4])
+        print(open(argv[2]).read())
+        return 0
+    if len(argv) >= 9 and argv[0] == "traffic":
+        summarize_traffic(argv[1], argv[2], argv[3], argv[4], argv[5], argv[6], int(argv[7]), argv[8])
+        print(open(argv[2]).read())
+        return 0
+    print(__doc__, file=sys.stderr)
+    return 2
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

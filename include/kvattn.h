@@ -169,6 +169,18 @@ int32_t kvattn_mla_split_tokens(int32_t batch, int32_t num_heads, int32_t max_se
                                 int32_t block_size, int32_t split_tokens);
 
 /*
+ * Measurement utility: the next kvattn_gqa_decode or kvattn_mla_decode call
+ * made on the calling thread records `start_event` when its split-K kernel
+ * (the kernel that reads the cache) starts executing and `stop_event` when it
+ * ends, so the caller can time that kernel alone with hipEventElapsedTime.
+ * Both are hipEvent_t handles the caller created with timing enabled (both
+ * non-NULL, or both NULL to disarm).  The setting is consumed by that next
+ * call whether or not it succeeds; the log-sum-exp merge kernel the call may
+ * add afterwards is outside the two events.
+ */
+kvattn_status kvattn_time_next_kernel(void* start_event, void* stop_event);
+
+/*
  * Measurement utility, not part of the attention path: stream `bytes` bytes
  * of device memory at `buf` through 16-byte loads with `workgroups`
  * workgroups of 256 threads, to measure the device's practical HBM read

@@ -150,3 +150,16 @@ def test_python_binding_rejects_cpu_tensors():
     kv = torch.zeros(1, 2, 16, 128)
     with pytest.raises(ValueError):
         K.gqa_decode(q, kv, kv, torch.zeros(1, dtype=torch.int32), 0.1)
+
+
+def test_time_next_kernel_arms_both_events_or_none():
+    """The timing hook only stores the two event handles; a half-armed pair is rejected on the host."""
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.kvattn_time_next_kernel(fake, None) == K.KVATTN_ERR_INVALID
+    assert lib.kvattn_time_next_kernel(None, fake) == K.KVATTN_ERR_INVALID
+    assert lib.kvattn_time_next_kernel(None, None) == K.KVATTN_OK
+    # A rejected decode call consumes (disarms) an armed pair without launching anything.
+    assert lib.kvattn_time_next_kernel(fake, fake) == K.KVATTN_OK
+    st = lib.kvattn_gqa_decode(None, None, None, None, None, None, None, 1, 8, 2, 128, 16, 0, 0, 16, 0.1,
+                               K.KVATTN_BF16, 0, None, 0, None)
+    assert st == K.KVATTN_ERR_INVALID
