@@ -126,7 +126,9 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
                                 void* stream);
 
 /* Workspace bytes kvattn_gqa_decode needs for these arguments (0 when no split is needed).
- * Returns (size_t)-1 for arguments kvattn_gqa_decode would reject. */
+ * block_size is 0 for a contiguous cache (block_table == NULL) and the pool's block size for a
+ * paged one: the split planner treats the two differently.  Returns (size_t)-1 for arguments
+ * kvattn_gqa_decode would reject. */
 size_t kvattn_gqa_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, int32_t block_size,
                                   int32_t split_tokens, kvattn_dtype dtype);
@@ -162,7 +164,11 @@ size_t kvattn_mla_workspace_bytes(int32_t batch, int32_t num_heads, int32_t d_la
                                   int32_t d_rope, int32_t max_seq_len, int32_t block_size,
                                   int32_t split_tokens, kvattn_dtype dtype);
 
-/* The split size (tokens per split) a call with these arguments uses. */
+/* The split size (tokens per split) a call with these arguments uses (block_size 0 for a
+ * contiguous cache, as for the workspace queries).  split_tokens = 0 asks for the library's choice:
+ * for a contiguous GQA cache the fewest splits that still give every compute unit two resident
+ * workgroups; for a paged one (ragged lengths assumed) about four workgroups per compute unit of
+ * at most 2048 tokens each; for MLA about one 128-head workgroup per compute unit. */
 int32_t kvattn_gqa_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t max_seq_len, int32_t block_size, int32_t split_tokens);
 int32_t kvattn_mla_split_tokens(int32_t batch, int32_t num_heads, int32_t max_seq_len,

@@ -113,9 +113,17 @@ def test_split_planner():
     assert f(2, 8, 2, 4096, 0, 192) == 192          # an explicit request wins
     for B, h, g, S in [(16, 32, 8, 8192), (8, 64, 64, 8192), (64, 64, 8, 8192), (64, 64, 1, 8192),
                        (128, 64, 8, 32768), (1, 8, 2, 512), (3, 4, 4, 1)]:
-        s = f(B, h, g, S, 0, 0)
-        assert s > 0 and s % 64 == 0 and s <= max(2048, 64)
-    assert f(16, 32, 8, 8192, 0, 0) == 1024
+        for bs in (0, 16):
+            s = f(B, h, g, S, bs, 0)
+            assert s > 0 and s % 64 == 0 and s <= max(S + 63, 256)
+            if bs:
+                assert s <= 2048  # paged: bounded split length for ragged sequences
+    # contiguous: fewest splits giving 2 workgroups per CU (512 in all) on the measured shapes
+    assert f(16, 32, 8, 8192, 0, 0) == 2048       # 128 (sequence, KV head) units x 4 splits
+    assert f(64, 64, 1, 8192, 0, 0) == 1024       # 64 units x 8
+    assert f(64, 64, 8, 8192, 0, 0) == 8192       # 512 units, no split
+    assert f(8, 64, 64, 8192, 0, 0) == 8192
+    assert f(128, 64, 8, 32768, 16, 0) == 2048    # paged
     m = lib.kvattn_mla_split_tokens
     assert m(32, 128, 8192, 0, 0) == 1024
     assert m(32, 128, 8192, 0, 512) == 512
