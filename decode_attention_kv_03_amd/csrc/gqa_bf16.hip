@@ -133,9 +133,11 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
     for (int i = tid; i < count; i += 256) tbl[i] = table_row[first + i];
     win_first = first;
   };
-  if (paged && n_tiles > 0) load_window(t_begin / bs);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries and table land before any copy is issued
-  __syncthreads();
+  if (paged) {
+    if (n_tiles > 0) load_window(t_begin / bs);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the table lands before any copy is addressed
+    __syncthreads();
+  }
 
   f32x4 acc[HBW][8];
   float m_ref[HBW], l_run[HBW];
@@ -202,6 +204,11 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
     voff[db] = kTileB + vrow * kRowB + 16 * ((2 * db + ((n16 & 3) >> 1)) ^ swz(vrow)) + 8 * (n16 & 1);
 
   for (int s = 0; s < NST - 1 && s < n_tiles; ++s) issue_tile(t_begin + s * kTile, s);
+  // The queries and the first tiles were fetched together (one HBM latency at
+  // start-up, not two).  Let them all land here: the compiler cannot see the
+  // copies in the vector-memory counter, and a wait it placed on the query
+  // loads inside the loop would drain the copies in flight every tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   for (int it = 0; it < n_tiles; ++it) {
     // Tile `it` must have landed; the ones issued after it may stay in flight.

@@ -150,10 +150,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
       qf[j] = __builtin_bit_cast(
           bf16x8, *reinterpret_cast<const u32x4*>(qb + (int64_t)head * kRowElems + 8 * (4 * j + 2 * half + g)));
   }
-  // Let the query loads land now: the compiler cannot see the tile copies in
-  // the vector-memory counter, and any wait it places on these loads inside
-  // the loop would also drain the copies in flight.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   f32x16 acc[kColBlocks];
 #pragma unroll
@@ -261,6 +257,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   const int ntok = t_end - t_begin;
   const int n_tiles = ntok > 0 ? (ntok + kT - 1) / kT : 0;
   if (n_tiles > 0) issue_tile(t_begin, 0);
+  // The queries and the first tile were fetched together (one HBM latency at
+  // start-up, not two).  Let both land here: the compiler cannot see the
+  // copies in the vector-memory counter, and a wait it placed on the query
+  // loads inside the loop would drain the copies in flight every tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   if (n_tiles > 1) issue_tile(t_begin + kT, 1);
 
   // One tile: wait for its copies, issue the copies of tile it+2, scores,
