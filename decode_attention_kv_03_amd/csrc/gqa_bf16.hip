@@ -63,6 +63,15 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory");
 }
 
+// The same copy addressed as a wave-uniform 64-bit base plus a per-lane
+// 32-bit byte offset, so the per-tile address arithmetic is scalar.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
 // Wait until at most `N` of this wave's copies are outstanding, then
 // synchronise the workgroup (LDS reads of every wave complete first).
 template <int N>
@@ -158,7 +167,18 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
   // instruction i writes LDS slot (row 4*(i%16) + l/16, chunk l%16), which
   // holds logical chunk (l%16) ^ swz(row).  Rows past the split's end
   // re-read its last row (masked out of the softmax).
-  auto issue_tile = [&](int t0, int stage) {
+  // Per-lane byte offsets of the paged fast path: lane l of an instruction
+  // with row group rg copies row 4*rg + l/16 (l/16-th of its four rows), slot
+  // l%16, which holds logical chunk (l%16) ^ swz(row); swz depends on rg mod 4
+  // only (rows of one wave's instructions are 32*(wave&1) + 4*u + l/16).
+  const bool paged_fast = paged && a.block_shift >= 2;
+  uint32_t dpo[4];
+#pragma unroll
+  for (int u4 = 0; u4 < 4; ++u4) {
+    const int row = 4 * u4 + (lane >> 4);
+    dpo[u4] = (uint32_t)(((lane >> 4) * kHeadDim + ((lane & 15) ^ swz(row)) * 8) * 2);
+  }
+  auto issue_tile = [&](int t0, int stage) __attribute__((always_inline)) {
     if (paged && (min(t0 + kTile, t_end) - 1) / bs >= win_first + kTblSlots) {
       // slow path: slide the table window (drains the copies in flight)
       __builtin_amdgcn_s_waitcnt(0x0070);
@@ -168,6 +188,36 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
       __syncthreads();
     }
     const uint32_t stage_base = (uint32_t)(uintptr_t)&ring[stage][0];
+    if (paged_fast && t0 + kTile <= t_end) {
+      // Paged, full tile, power-of-two block size >= 4: an instruction's four
+      // rows start at a multiple of 4 tokens and so lie in one block.  Its
+      // table entry is a wave-uniform scalar load (counted by lgkmcnt, so the
+      // copies in flight are left alone) and its address one scalar base plus
+      // a per-lane offset fixed for the kernel (dpo, by instruction mod 4).
+      const int tw = t0 + 32 * (wave & 1);  // first token of this wave's 8 instructions
+      const int32_t* ep[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ep[u] = table_row + ((tw + 4 * u) >> a.block_shift);
+      int e[8];
+      asm volatile(
+          "s_load_dword %0, %8, 0x0\n\ts_load_dword %1, %9, 0x0\n\ts_load_dword %2, %10, 0x0\n\t"
+          "s_load_dword %3, %11, 0x0\n\ts_load_dword %4, %12, 0x0\n\ts_load_dword %5, %13, 0x0\n\t"
+          "s_load_dword %6, %14, 0x0\n\ts_load_dword %7, %15, 0x0\n\ts_waitcnt lgkmcnt(0)"
+          : "=&s"(e[0]), "=&s"(e[1]), "=&s"(e[2]), "=&s"(e[3]), "=&s"(e[4]), "=&s"(e[5]), "=&s"(e[6]), "=&s"(e[7])
+          : "s"(ep[0]), "s"(ep[1]), "s"(ep[2]), "s"(ep[3]), "s"(ep[4]), "s"(ep[5]), "s"(ep[6]), "s"(ep[7])
+          : "memory");
+      const uint16_t* tbase = (wave >> 1) == 0 ? kbase : vbase;  // waves 0-1 copy K, 2-3 copy V
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int inst = wave * 8 + u;
+        const int tg = tw + 4 * u;  // first token of the instruction's four rows
+        const int64_t row0 = (e[u] >= 0 && (int64_t)e[u] < a.cache_len)
+                                 ? ((int64_t)e[u] * a.num_kv_heads + j) * bs + (tg & (bs - 1))
+                                 : 0;  // out-of-range entry: in-bounds stand-in rows
+        dma16s(dpo[u & 3], tbase + row0 * kHeadDim, stage_base + (inst >> 4) * kTileB + (inst & 15) * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int inst = wave * 8 + u;
