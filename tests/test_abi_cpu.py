@@ -129,6 +129,12 @@ def test_split_planner():
     assert m(32, 128, 8192, 0, 512) == 512
 
 
+def test_mla_workspace_bytes():
+    # 8 splits of fp32 partial outputs (512 wide) and log-sum-exps per (sequence, head)
+    assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 8192, 0, 0, K.KVATTN_BF16) == 32 * 128 * 8 * 513 * 4
+    assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 1024, 0, 1024, K.KVATTN_BF16) == 0  # one split
+
+
 @pytest.mark.parametrize(
     "kw,status",
     [
