@@ -16,6 +16,10 @@ Sources (page title, then section):
 * "Why GQA's KV Cache Savings Don't Fully Reduce TPOT", section "What Makes
   MLA Different": the absorbed form needs no reconstruction, and the 64-wide
   RoPE part is kept and used explicitly (cache row width 512 + 64).
+* "One dial, four settings" (runbooks, Document 07), the full ladder's SWA
+  row and the question on sliding-window attention: with a window of W
+  tokens each token attends only to the last W, and tokens outside the
+  window are not attended at all (``window`` below; 0 means no window).
 * "Compressing the KV Cache ... (MLA) vs. Meta's Grouped Queries (GQA)",
   section "KV-Cache Management Guardrails": caches live in fixed-size blocks
   (paged attention); the pages give no block layout, so the layout below is
@@ -68,7 +72,12 @@ def attend(q, K, V, scale):
     return o, m + np.log(z)
 
 
-def gqa_decode(q, K, V, seq_lens, scale, bf16=False):
+def window_start(n, window):
+    """First attended token of a sequence of ``n`` tokens: the last ``window`` tokens (window 0: all)."""
+    return max(0, n - window) if window > 0 else 0
+
+
+def gqa_decode(q, K, V, seq_lens, scale, bf16=False, window=0):
     """Grouped-query decode: ``h`` query heads over ``g`` cached K/V heads.
 
     q: [B, h, d]; K: [B, g, S, d]; V: [B, g, S, d_v]; seq_lens: [B].
@@ -76,7 +85,8 @@ def gqa_decode(q, K, V, seq_lens, scale, bf16=False):
     and MLA": index, never repeat), so the heads of one group are the
     contiguous run ``j*(h/g) .. (j+1)*(h/g)-1`` (section 3 figure).  ``g = h``
     is MHA, ``g = 1`` is MQA.  Sequence ``b`` attends to its first
-    ``seq_lens[b]`` cached tokens.  Returns (o [B, h, d_v], lse [B, h]).
+    ``seq_lens[b]`` cached tokens, or with ``window`` > 0 to the last
+    ``window`` of them.  Returns (o [B, h, d_v], lse [B, h]).
     With ``bf16=True`` the arrays hold bfloat16 bit patterns.
     """
     B, h, _ = q.shape
@@ -89,9 +99,10 @@ def gqa_decode(q, K, V, seq_lens, scale, bf16=False):
     lse = np.full((B, h), -np.inf, dtype=np.float64)
     for b in range(B):
         n = int(seq_lens[b])
+        t0 = window_start(n, window)
         qb = _f64(q[b], bf16)
-        Kb = _f64(K[b, :, :n], bf16)
-        Vb = _f64(V[b, :, :n], bf16)
+        Kb = _f64(K[b, :, t0:n], bf16)
+        Vb = _f64(V[b, :, t0:n], bf16)
         for i in range(h):
             j = i // r
             o[b, i], lse[b, i] = attend(qb[i], Kb[j], Vb[j], scale)
@@ -116,7 +127,7 @@ def paged_gather(pool, table_row, n, block_size, kv_head=None):
     return np.stack(rows)
 
 
-def paged_gqa_decode(q, K_pool, V_pool, block_table, seq_lens, block_size, scale, bf16=False):
+def paged_gqa_decode(q, K_pool, V_pool, block_table, seq_lens, block_size, scale, bf16=False, window=0):
     """``gqa_decode`` with K/V in a block pool addressed through ``block_table`` [B, max_blocks]."""
     B, h, _ = q.shape
     g = K_pool.shape[1]
@@ -129,8 +140,9 @@ def paged_gqa_decode(q, K_pool, V_pool, block_table, seq_lens, block_size, scale
     for b in range(B):
         n = int(seq_lens[b])
         qb = _f64(q[b], bf16)
-        Kb = [_f64(paged_gather(K_pool, block_table[b], n, block_size, j), bf16) for j in range(g)]
-        Vb = [_f64(paged_gather(V_pool, block_table[b], n, block_size, j), bf16) for j in range(g)]
+        t0 = window_start(n, window)
+        Kb = [_f64(paged_gather(K_pool, block_table[b], n, block_size, j)[t0:], bf16) for j in range(g)]
+        Vb = [_f64(paged_gather(V_pool, block_table[b], n, block_size, j)[t0:], bf16) for j in range(g)]
         for i in range(h):
             j = i // r
             o[b, i], lse[b, i] = attend(qb[i], Kb[j], Vb[j], scale)
