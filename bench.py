@@ -56,6 +56,8 @@ def algorithmic(w, lens):
     """
     import numpy as np
 
+    if getattr(w, "window", 0):
+        lens = np.minimum(lens, w.window)  # a sliding window reads only its last `window` tokens
     ntok = int(np.sum(lens))
     if hasattr(w, "num_kv_heads"):
         eb = 4 if w.dtype == "f32" else 2
@@ -112,9 +114,9 @@ def cpu_baseline(w, x, seconds):
         if hasattr(w, "num_kv_heads"):
             if w.paged:
                 oracle.paged_gqa_decode(q[b:b + 1], args[0], args[1], args[2], lens[b:b + 1], w.block_size, w.scale,
-                                        bf16=bf16)
+                                        bf16=bf16, window=w.window)
             else:
-                oracle.gqa_decode(q[b:b + 1], args[0], args[1], lens[b:b + 1], w.scale, bf16=bf16)
+                oracle.gqa_decode(q[b:b + 1], args[0], args[1], lens[b:b + 1], w.scale, bf16=bf16, window=w.window)
         else:
             oracle.mla_absorbed_decode(q[b:b + 1], args[0], lens[b:b + 1], w.scale, d_c=w.d_latent, bf16=bf16)
         t_total += time.perf_counter() - t0
@@ -192,8 +194,9 @@ def main():
     x0 = make(w, dev)
     lens = W.host_view(x0["seq_lens"])
     nbytes, flops = algorithmic(w, lens)
-    cache_bytes = sum(t.numel() * t.element_size() for k, t in x0.items() if k in ("k", "v", "cache"))
-    copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(cache_bytes, 1))))
+    # Enough copies of the cache that the bytes one step reads cycle through at least 1 GiB (no step
+    # finds its data in the 256 MB last-level cache); a sliding window reads only part of its cache.
+    copies = max(1, min(8, math.ceil(ROTATE_BYTES / max(nbytes, 1))))
     xs = [x0]
     for c in range(1, copies):
         xc = dict(x0)
@@ -220,7 +223,8 @@ def main():
         x = xs[i % copies]
         if is_gqa:
             gqa_decode(x["q"], x["k"], x["v"], x["seq_lens"], w.scale, block_table=x["block_table"],
-                       max_seq_len=max_len, out=out, split_tokens=args.split_tokens, workspace=ws, stream=stream)
+                       max_seq_len=max_len, out=out, split_tokens=args.split_tokens, workspace=ws, stream=stream,
+                       window=w.window)
         else:
             mla_decode(x["q"], x["cache"], x["seq_lens"], w.scale, block_table=x["block_table"], max_seq_len=max_len,
                        out=out, split_tokens=args.split_tokens, workspace=ws, stream=stream)
@@ -299,7 +303,7 @@ def main():
            "rotated_input_copies": copies, "split_tokens": args.split_tokens or "auto"}
     if is_gqa:
         cfg.update({"num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                    "block_size": w.block_size})
+                    "block_size": w.block_size, "window": w.window})
     else:
         cfg.update({"num_heads": w.num_heads, "d_latent": w.d_latent, "d_rope": w.d_rope, "block_size": w.block_size})
     line = {

@@ -223,17 +223,35 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
                                 int32_t num_kv_heads, int32_t head_dim, int64_t cache_len, int32_t block_size,
                                 int32_t max_blocks_per_seq, int32_t max_seq_len, float scale, kvattn_dtype dtype,
                                 int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  return kvattn_gqa_decode_window(q, k_cache, v_cache, block_table, seq_lens, out, lse, batch, num_q_heads,
+                                  num_kv_heads, head_dim, cache_len, block_size, max_blocks_per_seq, max_seq_len,
+                                  scale, 0, dtype, split_tokens, workspace, workspace_bytes, stream);
+}
+
+kvattn_status kvattn_gqa_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int64_t cache_len, int32_t block_size, int32_t max_blocks_per_seq,
+                                       int32_t max_seq_len, float scale, int32_t window, kvattn_dtype dtype,
+                                       int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
   const kvattn::LaunchEvents ev = take_timing_events();  // armed for this call only, whatever its outcome
   kvattn_status st = check_gqa(q, k_cache, v_cache, seq_lens, out, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                                scale);
   if (st != KVATTN_OK) return st;
+  if (window < 0) return fail(KVATTN_ERR_INVALID, "window must be >= 0 (0: attend to all tokens), got %lld", window);
   const bool paged = block_table != nullptr;
   if ((st = check_cache_geometry(cache_len, block_size, max_blocks_per_seq, max_seq_len, paged)) != KVATTN_OK)
     return st;
   if ((st = check_split(split_tokens)) != KVATTN_OK) return st;
 
-  const int32_t split = plan_gqa_split(batch, num_q_heads, num_kv_heads, max_seq_len, paged, split_tokens);
-  const int32_t nsplit = n_splits(max_seq_len, split);
+  // A window needs only the tokens from the 64-aligned token below its start:
+  // at most window + 63 per sequence.  Splits are planned for that span (the
+  // planners give no more splits for a shorter span, so the workspace query
+  // for the full context still bounds this call's needs; the check below
+  // guards it).
+  const int32_t span = window > 0 ? (int32_t)std::min<int64_t>(max_seq_len, (int64_t)window + 63) : max_seq_len;
+  const int32_t split = plan_gqa_split(batch, num_q_heads, num_kv_heads, span, paged, split_tokens);
+  const int32_t nsplit = n_splits(span, split);
   const size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
@@ -256,6 +274,7 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
   a.block_shift = paged ? pow2_shift(block_size) : -1;
   a.max_blocks = paged ? max_blocks_per_seq : 0;
   a.len_cap = max_seq_len;
+  a.window = window;
   a.split_tokens = split;
   a.n_split = nsplit;
   a.scale_log2 = scale * kvattn::kLog2eHost;

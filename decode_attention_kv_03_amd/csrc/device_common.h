@@ -80,6 +80,14 @@ __device__ __forceinline__ float wave_reduce_sum(float v) {
   return v;
 }
 
+// Sliding window ("One dial, four settings", the full ladder's SWA row and
+// the sliding-window question): a sequence of `len` tokens attends to its
+// last `window` tokens (window 0: all of them).  First attended token, and
+// the 64-aligned token the splits start from (tiles keep their alignment;
+// tokens below the first attended one are masked).
+__device__ __forceinline__ int window_first(int len, int window) { return window > 0 && len > window ? len - window : 0; }
+__device__ __forceinline__ int window_base(int len, int window) { return window_first(len, window) & ~63; }
+
 // Clamp a device-side sequence length into [0, cap].
 __device__ __forceinline__ int clamp_len(int len, int cap) { return len < 0 ? 0 : (len > cap ? cap : len); }
 

@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
   const int r = a.group, h = a.num_q_heads;
 
   const int len = clamp_len(a.seq_lens[b], a.len_cap);
-  const int t_begin = split * a.split_tokens;
+  const int t_lo = window_first(len, a.window);  // tokens before t_lo are outside the window
+  const int t_begin = window_base(len, a.window) + split * a.split_tokens;
   const bool final_out = (a.n_split == 1);
   if (!final_out && t_begin >= len) return;  // the merge only reads splits that hold tokens
   const int t_end = min(len, t_begin + a.split_tokens);
@@ -294,10 +295,12 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
         for (int sb = 0; sb < kSub; ++sb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) sv[4 * sb + v] = s[sb][v] * a.scale_log2;
-        if (t0 + u0 + kUnit > t_end) {
+        if (t0 + u0 + kUnit > t_end || t0 + u0 < t_lo) {
 #pragma unroll
-          for (int e = 0; e < 4 * kSub; ++e)
-            if (t0 + u0 + 16 * (e >> 2) + 4 * grp + (e & 3) >= t_end) sv[e] = -INFINITY;
+          for (int e = 0; e < 4 * kSub; ++e) {
+            const int t = t0 + u0 + 16 * (e >> 2) + 4 * grp + (e & 3);
+            if (t >= t_end || t < t_lo) sv[e] = -INFINITY;
+          }
         }
         float mt = sv[0];
 #pragma unroll
@@ -312,10 +315,13 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
 #pragma unroll
           for (int db = 0; db < 8; ++db) acc[hbi][db] *= alpha;
         }
+        // m_ref stays -inf while every token so far lay before a sliding
+        // window; its probabilities are then 0 (not -inf - -inf = NaN).
+        const float m_use = m_ref[hbi] == -INFINITY ? 0.f : m_ref[hbi];
         uint32_t pk[2 * kSub];
 #pragma unroll
         for (int e = 0; e < 2 * kSub; ++e) {
-          pk[e] = pack_bf16x2(fast_exp2(sv[2 * e] - m_ref[hbi]), fast_exp2(sv[2 * e + 1] - m_ref[hbi]));
+          pk[e] = pack_bf16x2(fast_exp2(sv[2 * e] - m_use), fast_exp2(sv[2 * e + 1] - m_use));
           l_run[hbi] = add_bf16x2(pk[e], l_run[hbi]);  // normalise with the weights the matrix core sees
         }
         const int vbase_off = u0 * kRowB;

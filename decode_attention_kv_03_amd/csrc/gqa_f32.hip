@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void gqa_split_f32(DecodeArgs a) {
   const int r = a.group, h = a.num_q_heads;
 
   const int len = clamp_len(a.seq_lens[b], a.len_cap);
-  const int t_begin = split * a.split_tokens;
+  const int t_lo = window_first(len, a.window);  // tokens before t_lo are outside the window
+  const int t_begin = window_base(len, a.window) + split * a.split_tokens;
   const bool final_out = (a.n_split == 1);
   if (!final_out && t_begin >= len) return;
   const int t_end = min(len, t_begin + a.split_tokens);
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void gqa_split_f32(DecodeArgs a) {
         dot = fmaf(x.z, y.z, dot);
         dot = fmaf(x.w, y.w, dot);
       }
-      sc[i][tt] = (t0 + tt < t_end) ? dot * a.scale_log2 : -INFINITY;
+      sc[i][tt] = (t0 + tt < t_end && t0 + tt >= t_lo) ? dot * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
 
@@ -101,11 +102,12 @@ __global__ __launch_bounds__(256) void gqa_split_f32(DecodeArgs a) {
       float mt = -INFINITY;
       for (int tt = 0; tt < kTileF; ++tt) mt = fmaxf(mt, sc[i][tt]);
       const float m_old = m_s[i];
-      const float m_new = fmaxf(m_old, mt);  // finite: every tile holds a valid token
-      const float al = fast_exp2(m_old - m_new);
+      const float m_new = fmaxf(m_old, mt);  // -inf only while every token so far was masked (sliding window)
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // then al and every p are 0, not NaN
+      const float al = fast_exp2(m_old - m_use);
       float sum = 0.f;
       for (int tt = 0; tt < kTileF; ++tt) {
-        const float p = fast_exp2(sc[i][tt] - m_new);
+        const float p = fast_exp2(sc[i][tt] - m_use);
         sc[i][tt] = p;
         sum += p;
       }

@@ -41,6 +41,7 @@ struct DecodeArgs {
   int32_t block_shift;      // paged: log2(block_size) when it is a power of two, else -1
   int32_t max_blocks;       // paged: block_table row length
   int32_t len_cap;          // device lengths are clamped to [0, len_cap]
+  int32_t window;           // GQA sliding window: attend to the last `window` tokens (0: all)
   int32_t split_tokens;     // tokens per split (multiple of 64)
   int32_t n_split;          // splits per sequence in the grid
   float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units

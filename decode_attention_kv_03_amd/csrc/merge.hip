@@ -18,7 +18,7 @@ template <int DV, bool BF16_OUT>
 __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
   const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int len = clamp_len(a.seq_lens[b], a.len_cap);
-  int nv = (len + a.split_tokens - 1) / a.split_tokens;
+  int nv = (len - window_base(len, a.window) + a.split_tokens - 1) / a.split_tokens;
   nv = min(nv, a.n_split);
   const int64_t row = (int64_t)b * a.num_q_heads + head;
   const float* pl = a.part_lse + row * a.n_split;

@@ -27,6 +27,11 @@ SIGNATURES = {
         [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
          _c_i32, _c_f32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
     ),
+    "kvattn_gqa_decode_window": (
+        _c_i32,
+        [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
+         _c_i32, _c_f32, _c_i32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
+    ),
     "kvattn_gqa_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_mla_decode": (
         _c_i32,
@@ -168,14 +173,15 @@ def _workspace(nbytes, workspace, device):
 
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, scale, *, block_table=None, max_seq_len=None, out=None,
-               return_lse=False, lse=None, split_tokens=0, workspace=None, stream=None):
+               return_lse=False, lse=None, split_tokens=0, workspace=None, stream=None, window=0):
     """Grouped-query decode attention (MHA at g = h, MQA at g = 1).
 
     q [B, h, d]; contiguous k_cache/v_cache [B, g, S, d], or, with
     ``block_table`` (int32 [B, max_blocks]), block pools [N, g, block_size, d];
     seq_lens int32 [B].  ``max_seq_len`` bounds every length (default: S, or
-    max_blocks * block_size).  Returns out [B, h, d] (and lse [B, h] fp32
-    when ``return_lse``).
+    max_blocks * block_size).  ``window`` > 0 attends only to each sequence's
+    last ``window`` tokens (kvattn_gqa_decode_window).  Returns out [B, h, d]
+    (and lse [B, h] fp32 when ``return_lse``).
     """
     _need_gpu(q, k_cache, v_cache, seq_lens, block_table, out, lse, workspace)
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
@@ -210,10 +216,16 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale, *, block_table=None, max_se
     if nbytes == ctypes.c_size_t(-1).value:
         nbytes = 0  # the decode call reports the precise problem
     ws = _workspace(nbytes, workspace, q.device)
-    _check(lib.kvattn_gqa_decode(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
-        B, h, g, d, cache_len, block_size, max_blocks, max_seq_len, float(scale), code, int(split_tokens),
-        _ptr(ws), nbytes, _stream(stream)))
+    if window:
+        _check(lib.kvattn_gqa_decode_window(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+            B, h, g, d, cache_len, block_size, max_blocks, max_seq_len, float(scale), int(window), code,
+            int(split_tokens), _ptr(ws), nbytes, _stream(stream)))
+    else:
+        _check(lib.kvattn_gqa_decode(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+            B, h, g, d, cache_len, block_size, max_blocks, max_seq_len, float(scale), code, int(split_tokens),
+            _ptr(ws), nbytes, _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

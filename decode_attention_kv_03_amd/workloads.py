@@ -34,6 +34,7 @@ class GqaWorkload:
     seed: int
     scale: float
     block_size: int = 0  # 0: contiguous cache [B, g, S, d]; else pool [num_blocks, g, block_size, d]
+    window: int = 0  # sliding window: attend to the last `window` tokens (0: all)
 
     @property
     def paged(self):
@@ -67,6 +68,9 @@ WORKLOADS = {
         GqaWorkload("llama3_70b_gqa_h64_g8_b64_s8192", 64, 64, 8, 128, 8192, "bf16", 32, 1 / math.sqrt(128)),
         GqaWorkload("llama3_70b_mqa_h64_g1_b64_s8192", 64, 64, 1, 128, 8192, "bf16", 33, 1 / math.sqrt(128)),
         GqaWorkload("paged_gqa_h64_g8_b128_bs16_len1_32768", 128, 64, 8, 128, 32768, "bf16", 4, 1 / math.sqrt(128), 16),
+        # Sliding-window decode at Mistral-7B v0.1's shape (h=32, g=8, window 4096) over 32K-token sequences.
+        GqaWorkload("mistral7b_swa_h32_g8_b16_s32768_w4096", 16, 32, 8, 128, 32768, "bf16", 6, 1 / math.sqrt(128),
+                    window=4096),
         MlaWorkload("deepseek_v2_mla_h128_b32_s8192", 32, 128, 8192, 5, 1 / math.sqrt(192)),
     ]
 }

@@ -125,6 +125,25 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
                                 int32_t split_tokens, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * Grouped-query decode with a sliding window: each sequence attends only to
+ * its last `window` cached tokens, t in [max(0, seq_lens[b] - window),
+ * seq_lens[b]) ("One dial, four settings": the full ladder's SWA row and the
+ * sliding-window question, where a token outside the window is not attended
+ * at all).  window = 0 attends to every token and is kvattn_gqa_decode.
+ * Arguments and layouts are those of kvattn_gqa_decode (token indices and
+ * block-table lookups stay absolute); the workspace kvattn_gqa_workspace_bytes
+ * reports for the same arguments is enough.  window < 0 is KVATTN_ERR_INVALID.
+ */
+kvattn_status kvattn_gqa_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens, void* out,
+                                       float* lse, int32_t batch, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int64_t cache_len,
+                                       int32_t block_size, int32_t max_blocks_per_seq,
+                                       int32_t max_seq_len, float scale, int32_t window,
+                                       kvattn_dtype dtype, int32_t split_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 /* Workspace bytes kvattn_gqa_decode needs for these arguments (0 when no split is needed).
  * block_size is 0 for a contiguous cache (block_table == NULL) and the pool's block size for a
  * paged one: the split planner treats the two differently.  Returns (size_t)-1 for arguments

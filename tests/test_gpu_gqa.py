@@ -39,7 +39,7 @@ def assert_close(got, ref, dtype, what=""):
     return err.max()
 
 
-def reference(x, rows=None):
+def reference(x, rows=None, window=0):
     """fp64 oracle on the host copy of x (optionally only some sequences)."""
     w = x["workload"]
     bf16 = w.dtype == "bf16"
@@ -51,10 +51,11 @@ def reference(x, rows=None):
         bt = W.host_view(x["block_table"])
         k = W.host_view(x["k"])
         v = W.host_view(x["v"])
-        return oracle.paged_gqa_decode(q[rows], k, v, bt[rows], lens[rows], w.block_size, w.scale, bf16=bf16)
+        return oracle.paged_gqa_decode(q[rows], k, v, bt[rows], lens[rows], w.block_size, w.scale, bf16=bf16,
+                                       window=window)
     k = np.stack([W.host_view(x["k"][b]) for b in rows])
     v = np.stack([W.host_view(x["v"][b]) for b in rows])
-    return oracle.gqa_decode(q[rows], k, v, lens[rows], w.scale, bf16=bf16)
+    return oracle.gqa_decode(q[rows], k, v, lens[rows], w.scale, bf16=bf16, window=window)
 
 
 def run(x, **kw):
@@ -203,6 +204,7 @@ def test_rerun_is_bit_identical():
 
 FULL = [
     ("llama3_8b_gqa_h32_g8_b16_s8192", [0, 7, 15]),
+    ("mistral7b_swa_h32_g8_b16_s32768_w4096", [0, 9]),
     ("llama3_70b_mha_h64_g64_b8_s8192", [0, 5]),
     ("llama3_70b_gqa_h64_g8_b64_s8192", [0, 31, 63]),
     ("llama3_70b_mqa_h64_g1_b64_s8192", [0, 40, 63]),
@@ -215,8 +217,8 @@ def test_full_size_workloads_sampled(name, rows):
     w = W.WORKLOADS[name]
     note(name)
     x = W.make_gqa_inputs(w, DEV)
-    out, lse = run(x)
-    ref, ref_lse = reference(x, rows=rows)
+    out, lse = run(x, window=w.window)
+    ref, ref_lse = reference(x, rows=rows, window=w.window)
     assert_close(out[rows].float().cpu().numpy(), ref, "bf16", name)
     np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
     # every output is finite and every softmax average lies within the V range
@@ -238,3 +240,43 @@ def test_paged_full_size_sampled():
     assert torch.isfinite(out.float()).all()
     del x
     torch.cuda.empty_cache()
+
+
+WINDOW_CASES = [
+    # B, h, g, lens, window, split_tokens, dtype
+    (3, 32, 8, [300, 64, 5], 100, 64, "bf16"),
+    (2, 64, 1, [777, 200], 129, 128, "bf16"),
+    (2, 16, 2, [1000, 999], 64, 0, "bf16"),
+    (1, 8, 8, [513], 1, 64, "bf16"),
+    (2, 32, 8, [50, 70], 100, 64, "bf16"),      # window longer than every sequence
+    (2, 128, 1, [700, 333], 257, 192, "bf16"),
+    (3, 8, 2, [100, 1, 37], 33, 64, "f32"),
+    (2, 64, 8, [260, 90], 70, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,h,g,lens,window,split,dtype", WINDOW_CASES)
+def test_sliding_window_contiguous(B, h, g, lens, window, split, dtype):
+    S = max(lens) + 3
+    w = W.GqaWorkload(f"win_{B}_{h}_{g}", B, h, g, 128, S, dtype, 2000 + h + window, 1 / np.sqrt(128))
+    note(f"window={window} B={B} h={h} g={g} lens={lens} split={split} {dtype}")
+    x = W.make_gqa_inputs(w, DEV, lens=lens, poison_tail=True)
+    ref, ref_lse = reference(x, window=window)
+    out, lse = run(x, split_tokens=split, window=window)
+    assert_close(out.float().cpu().numpy(), ref, dtype, f"window={window}")
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=tol, rtol=1e-4)
+
+
+@pytest.mark.parametrize("block_size,window", [(16, 200), (16, 1000), (5, 77)])
+def test_sliding_window_paged(block_size, window):
+    pw = W.shrink(W.WORKLOADS["paged_gqa_h64_g8_b128_bs16_len1_32768"], batch=5, seq_len=900)
+    if block_size != 16:
+        pw = W.GqaWorkload("paged_win", 4, 16, 4, 128, 600, "bf16", 19, 0.1, block_size=block_size)
+    note(f"paged window={window} block_size={block_size}")
+    x = W.make_gqa_inputs(pw, DEV, poison_tail=True)
+    ref, ref_lse = reference(x, window=window)
+    for split in (0, 64, 256):
+        out, lse = run(x, split_tokens=split, window=window)
+        assert_close(out.float().cpu().numpy(), ref, "bf16", f"split={split}")
+        np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
