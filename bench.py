@@ -101,6 +101,12 @@ def cpu_baseline(w, x, seconds):
                 host[b] = (k, v, np.arange(nblk, dtype=np.int64)[None])
             else:
                 host[b] = (W.host_view(x["k"][b])[None], W.host_view(x["v"][b])[None], None)
+        elif w.paged:
+            bt = W.host_view(x["block_table"][b:b + 1])
+            nblk = (int(lens[b]) + w.block_size - 1) // w.block_size
+            ids = bt[0, :nblk]
+            host[b] = (W.host_view(x["cache"][torch_index(ids, x["cache"].device)]),
+                       np.arange(nblk, dtype=np.int64)[None])
         else:
             host[b] = (W.host_view(x["cache"][b])[None],)
         return host[b]
@@ -117,6 +123,9 @@ def cpu_baseline(w, x, seconds):
                                         bf16=bf16, window=w.window)
             else:
                 oracle.gqa_decode(q[b:b + 1], args[0], args[1], lens[b:b + 1], w.scale, bf16=bf16, window=w.window)
+        elif w.paged:
+            oracle.paged_mla_absorbed_decode(q[b:b + 1], args[0], args[1], lens[b:b + 1], w.block_size, w.scale,
+                                             d_c=w.d_latent, bf16=bf16)
         else:
             oracle.mla_absorbed_decode(q[b:b + 1], args[0], lens[b:b + 1], w.scale, d_c=w.d_latent, bf16=bf16)
         t_total += time.perf_counter() - t0

@@ -72,6 +72,9 @@ WORKLOADS = {
         GqaWorkload("mistral7b_swa_h32_g8_b16_s32768_w4096", 16, 32, 8, 128, 32768, "bf16", 6, 1 / math.sqrt(128),
                     window=4096),
         MlaWorkload("deepseek_v2_mla_h128_b32_s8192", 32, 128, 8192, 5, 1 / math.sqrt(192)),
+        # Paged latent cache: 64-token blocks, lengths uniform on [1, 16384], a random block permutation.
+        MlaWorkload("deepseek_v2_mla_paged_h128_b32_bs64_len1_16384", 32, 128, 16384, 7, 1 / math.sqrt(192),
+                    block_size=64),
     ]
 }
 

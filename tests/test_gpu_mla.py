@@ -121,3 +121,18 @@ def test_full_size_sampled():
     assert_close(out[rows].float().cpu().numpy(), ref, w.name)
     np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
     assert torch.isfinite(out.float()).all()
+
+
+def test_paged_full_size_sampled():
+    w = W.WORKLOADS["deepseek_v2_mla_paged_h128_b32_bs64_len1_16384"]
+    note(w.name)
+    x = W.make_mla_inputs(w, DEV)
+    out, lse = run(x)
+    lens = x["seq_lens"].cpu().numpy()
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 5})
+    ref, ref_lse = reference(x, rows=rows)
+    assert_close(out[rows].float().cpu().numpy(), ref, w.name)
+    np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    assert torch.isfinite(out.float()).all()
+    del x
+    torch.cuda.empty_cache()
