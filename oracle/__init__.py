@@ -15,6 +15,8 @@ float64, with NumPy matrix products as the only library step:
                      cached K/V rows; GQA/MHA/MQA head grouping; the paged
                      block-table gather; absorbed and explicit MLA; the
                      log-sum-exp merge of partial results.
+* ``fp8``         -- the E4M3 code decoder and decode attention over an fp8
+                     cache with one K and one V scale per KV head.
 * ``cache_bytes`` -- the KV-cache byte formulas and the decode-attention
                      arithmetic-intensity formula.
 
@@ -34,6 +36,13 @@ from .attention import (  # noqa: F401
     mla_absorb_query,
     mla_explicit_decode,
     lse_merge,
+)
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_to_f64,
+    dequantize_kv_heads,
+    gqa_decode_fp8,
+    paged_gqa_decode_fp8,
 )
 from .cache_bytes import (  # noqa: F401
     kv_cache_bytes,
