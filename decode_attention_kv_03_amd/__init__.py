@@ -5,7 +5,10 @@ Two operations, both hand-written HIP kernels behind a C ABI
 
 * ``gqa_decode`` -- grouped-query decode: ``h`` query heads share ``g``
   cached K/V heads (MHA when ``g = h``, MQA when ``g = 1``), over a
-  contiguous or block-table-paged cache with per-sequence lengths.
+  contiguous or block-table-paged cache with per-sequence lengths, optionally
+  restricted to a sliding window of the last tokens.
+* ``gqa_decode_fp8`` -- the same over an E4M3 (fp8) cache with one K and one
+  V scale per KV head.
 * ``mla_decode`` -- absorbed multi-head latent attention decode: every head
   scores an absorbed 576-wide query against cached ``[latent 512 | RoPE 64]``
   rows and accumulates its output in the 512-wide latent space.
@@ -19,6 +22,7 @@ raises if the library is missing or no GPU is present.
 from .kvattn import (  # noqa: F401
     KvattnError,
     gqa_decode,
+    gqa_decode_fp8,
     gqa_workspace_bytes,
     hbm_read_probe,
     library_path,

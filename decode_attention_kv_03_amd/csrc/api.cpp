@@ -168,6 +168,86 @@ kvattn_status hip_status(hipError_t e, const char* what) {
   return KVATTN_ERR_HIP;
 }
 
+// Cache operands of a GQA call: element type, and the per-KV-head scales of an fp8 cache.
+enum class CacheKind { kF32, kBf16, kFp8E4m3 };
+struct GqaCache {
+  const void* k;
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  CacheKind kind;
+};
+
+// Geometry checks, split planning and launches shared by the GQA entry points
+// (their operand checks have already run).
+kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCache& cache,
+                      const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t cache_len,
+                      int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
+                      int32_t window, int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  kvattn_status st;
+  if (window < 0) return fail(KVATTN_ERR_INVALID, "window must be >= 0 (0: attend to all tokens), got %lld", window);
+  const bool paged = block_table != nullptr;
+  if ((st = check_cache_geometry(cache_len, block_size, max_blocks_per_seq, max_seq_len, paged)) != KVATTN_OK)
+    return st;
+  if ((st = check_split(split_tokens)) != KVATTN_OK) return st;
+
+  // A window needs only the tokens from the 64-aligned token below its start:
+  // at most window + 63 per sequence.  Splits are planned for that span (the
+  // planners give no more splits for a shorter span, so the workspace query
+  // for the full context still bounds this call's needs; the check below
+  // guards it).
+  const int32_t span = window > 0 ? (int32_t)std::min<int64_t>(max_seq_len, (int64_t)window + 63) : max_seq_len;
+  const int32_t split = plan_gqa_split(batch, num_q_heads, num_kv_heads, span, paged, split_tokens);
+  const int32_t nsplit = n_splits(span, split);
+  const size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
+                workspace == nullptr ? 0 : (long long)workspace_bytes);
+
+  kvattn::DecodeArgs a{};
+  a.q = q;
+  a.k = cache.k;
+  a.v = cache.v;
+  a.k_scale = cache.k_scale;
+  a.v_scale = cache.v_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.cache_len = cache_len;
+  a.block_size = paged ? block_size : 0;
+  a.block_shift = paged ? pow2_shift(block_size) : -1;
+  a.max_blocks = paged ? max_blocks_per_seq : 0;
+  a.len_cap = max_seq_len;
+  a.window = window;
+  a.split_tokens = split;
+  a.n_split = nsplit;
+  a.scale_log2 = scale * kvattn::kLog2eHost;
+  a.ring_depth = KVATTN_GQA_RING_DEPTH;
+  if (nsplit > 1) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = a.part_o + (int64_t)batch * num_q_heads * nsplit * head_dim;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipErrorInvalidValue;
+  switch (cache.kind) {
+    case CacheKind::kF32: e = kvattn::launch_gqa_f32(a, s, ev); break;
+    case CacheKind::kBf16: e = kvattn::launch_gqa_bf16(a, s, ev); break;
+    case CacheKind::kFp8E4m3: e = kvattn::launch_gqa_fp8(a, s, ev); break;
+  }
+  if (e != hipSuccess) return hip_status(e, "split kernel launch");
+  if (nsplit > 1) {
+    e = kvattn::launch_merge(a, head_dim, cache.kind != CacheKind::kF32, s);
+    if (e != hipSuccess) return hip_status(e, "merge kernel launch");
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,59 +318,28 @@ kvattn_status kvattn_gqa_decode_window(const void* q, const void* k_cache, const
   kvattn_status st = check_gqa(q, k_cache, v_cache, seq_lens, out, batch, num_q_heads, num_kv_heads, head_dim, dtype,
                                scale);
   if (st != KVATTN_OK) return st;
-  if (window < 0) return fail(KVATTN_ERR_INVALID, "window must be >= 0 (0: attend to all tokens), got %lld", window);
-  const bool paged = block_table != nullptr;
-  if ((st = check_cache_geometry(cache_len, block_size, max_blocks_per_seq, max_seq_len, paged)) != KVATTN_OK)
-    return st;
-  if ((st = check_split(split_tokens)) != KVATTN_OK) return st;
+  const GqaCache cache{k_cache, v_cache, nullptr, nullptr, dtype == KVATTN_BF16 ? CacheKind::kBf16 : CacheKind::kF32};
+  return gqa_run(ev, q, cache, block_table, seq_lens, out, lse, batch, num_q_heads, num_kv_heads, head_dim,
+                 cache_len, block_size, max_blocks_per_seq, max_seq_len, scale, window, split_tokens, workspace,
+                 workspace_bytes, stream);
+}
 
-  // A window needs only the tokens from the 64-aligned token below its start:
-  // at most window + 63 per sequence.  Splits are planned for that span (the
-  // planners give no more splits for a shorter span, so the workspace query
-  // for the full context still bounds this call's needs; the check below
-  // guards it).
-  const int32_t span = window > 0 ? (int32_t)std::min<int64_t>(max_seq_len, (int64_t)window + 63) : max_seq_len;
-  const int32_t split = plan_gqa_split(batch, num_q_heads, num_kv_heads, span, paged, split_tokens);
-  const int32_t nsplit = n_splits(span, split);
-  const size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
-                workspace == nullptr ? 0 : (long long)workspace_bytes);
-
-  kvattn::DecodeArgs a{};
-  a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  a.lse = lse;
-  a.batch = batch;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = num_q_heads / num_kv_heads;
-  a.cache_len = cache_len;
-  a.block_size = paged ? block_size : 0;
-  a.block_shift = paged ? pow2_shift(block_size) : -1;
-  a.max_blocks = paged ? max_blocks_per_seq : 0;
-  a.len_cap = max_seq_len;
-  a.window = window;
-  a.split_tokens = split;
-  a.n_split = nsplit;
-  a.scale_log2 = scale * kvattn::kLog2eHost;
-  a.ring_depth = KVATTN_GQA_RING_DEPTH;
-  if (nsplit > 1) {
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = a.part_o + (int64_t)batch * num_q_heads * nsplit * head_dim;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == KVATTN_BF16 ? kvattn::launch_gqa_bf16(a, s, ev) : kvattn::launch_gqa_f32(a, s, ev);
-  if (e != hipSuccess) return hip_status(e, "split kernel launch");
-  if (nsplit > 1) {
-    e = kvattn::launch_merge(a, head_dim, dtype == KVATTN_BF16, s);
-    if (e != hipSuccess) return hip_status(e, "merge kernel launch");
-  }
-  return ok();
+kvattn_status kvattn_gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                    void* out, float* lse, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int64_t cache_len, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int32_t max_seq_len, float scale, int32_t window,
+                                    int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  const kvattn::LaunchEvents ev = take_timing_events();  // armed for this call only, whatever its outcome
+  // q/out are bf16: the bf16 checks (h/g <= 128) apply.
+  kvattn_status st = check_gqa(q, k_cache, v_cache, seq_lens, out, batch, num_q_heads, num_kv_heads, head_dim,
+                               KVATTN_BF16, scale);
+  if (st != KVATTN_OK) return st;
+  if (!k_scale || !v_scale) return fail(KVATTN_ERR_INVALID, "k_scale and v_scale must be non-null");
+  const GqaCache cache{k_cache, v_cache, k_scale, v_scale, CacheKind::kFp8E4m3};
+  return gqa_run(ev, q, cache, block_table, seq_lens, out, lse, batch, num_q_heads, num_kv_heads, head_dim,
+                 cache_len, block_size, max_blocks_per_seq, max_seq_len, scale, window, split_tokens, workspace,
+                 workspace_bytes, stream);
 }
 
 kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t* block_table, const int32_t* seq_lens,

@@ -33,6 +33,7 @@
 //    partial plus its log2-domain log-sum-exp for the merge kernel.
 #include "device_common.h"
 #include "kvattn_internal.h"
+#include "lds_copy.h"
 
 namespace kvattn {
 namespace {
@@ -51,36 +52,6 @@ constexpr float kRescaleSlack = 8.f;        // log2 units
 // r+16 share it; 16 consecutive rows get 16 distinct values and any 8
 // consecutive rows 8 distinct pairs, which is what the two read patterns need.
 __device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
-
-// 16-byte global -> LDS copy of every lane (lane i lands at lds_base + 16 i;
-// lds_base is wave-uniform and goes through M0), non-temporal.  Inline
-// assembly so later LDS reads are not treated as aliases of the copy; M0 is
-// written here and nowhere else in these kernels.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-
-// The same copy addressed as a wave-uniform 64-bit base plus a per-lane
-// 32-bit byte offset, so the per-tile address arithmetic is scalar.
-__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-
-// Wait until at most `N` of this wave's copies are outstanding, then
-// synchronise the workgroup (LDS reads of every wave complete first).
-template <int N>
-__device__ __forceinline__ void wait_copies_and_sync() {
-  static_assert(N == 0 || N == 8 || N == 16, "copy counts come in tiles of 8");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <int HBW, int WH, int NST>
 __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeArgs a) {

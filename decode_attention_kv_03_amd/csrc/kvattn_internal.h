@@ -26,6 +26,8 @@ struct DecodeArgs {
   const void* q;
   const void* k;            // GQA K, or the MLA latent rows
   const void* v;            // GQA V (unused by MLA)
+  const float* k_scale;     // fp8 GQA: per-KV-head scale of the K codes [g] (unused otherwise)
+  const float* v_scale;     // fp8 GQA: per-KV-head scale of the V codes [g]
   const int32_t* block_table;
   const int32_t* seq_lens;
   void* out;
@@ -56,6 +58,7 @@ struct LaunchEvents {
 
 hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
+hipError_t launch_gqa_fp8(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_hbm_read_probe(const void* buf, int64_t n16, uint32_t* sink, int workgroups, hipStream_t stream);
 // Log-sum-exp merge of the per-split partials into out/lse; d_v = 128 or 512.

@@ -44,6 +44,7 @@
 // per-lane order the scores come out in, so P^T needs no data movement.
 #include "device_common.h"
 #include "kvattn_internal.h"
+#include "lds_copy.h"
 
 namespace kvattn {
 namespace {
@@ -78,27 +79,6 @@ constexpr int kVDepth = MLA_VDEPTH;            // ... and value product
 __device__ __forceinline__ int lds_chunk(int row, int chunk) {
   const int r = row & 15;
   return (row >> 4) * (kTileBytes / 2) + (chunk >> 2) * 1024 + r * 64 + (((chunk & 3) ^ (r >> 2)) << 4);
-}
-
-// 16-byte global -> LDS copy of every lane: lane i's bytes land at
-// lds_base + 16 * i (lds_base is wave-uniform, taken through M0).  The
-// non-temporal hint marks the cache stream as read-once.  Issued as inline
-// assembly so the compiler does not treat every later LDS read as a possible
-// alias of the copy; M0 is written here and nowhere else in this kernel.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-
-// The same copy addressed as a wave-uniform 64-bit base plus a per-lane
-// 32-bit byte offset, so the per-tile address arithmetic is scalar.
-__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
 }
 
 struct TagFalse { static constexpr bool value = false; };

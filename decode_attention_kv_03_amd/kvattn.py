@@ -32,6 +32,11 @@ SIGNATURES = {
         [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
          _c_i32, _c_f32, _c_i32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
     ),
+    "kvattn_gqa_decode_fp8": (
+        _c_i32,
+        [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+         _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
+    ),
     "kvattn_gqa_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_mla_decode": (
         _c_i32,
@@ -172,6 +177,25 @@ def _workspace(nbytes, workspace, device):
     return workspace
 
 
+def _gqa_geometry(q, k_cache, block_table, max_seq_len):
+    """(g, cache_len, block_size, max_blocks, max_seq_len) of a GQA cache, checked against q [B, h, d]."""
+    B, h, d = q.shape
+    if block_table is None:
+        if k_cache.shape[0] != B or k_cache.shape[3] != d:
+            raise ValueError("kvattn: contiguous cache must be [B, g, S, d]")
+        g, cache_len, block_size, max_blocks = k_cache.shape[1], k_cache.shape[2], 0, 0
+        default_max = cache_len
+    else:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("kvattn: block_table must be int32 [B, max_blocks]")
+        if k_cache.shape[3] != d:
+            raise ValueError("kvattn: paged cache must be [num_blocks, g, block_size, d]")
+        g, cache_len, block_size, max_blocks = k_cache.shape[1], k_cache.shape[0], k_cache.shape[2], block_table.shape[1]
+        default_max = max_blocks * block_size
+    max_seq_len = default_max if max_seq_len is None else int(max_seq_len)
+    return g, cache_len, block_size, max_blocks, max_seq_len
+
+
 def gqa_decode(q, k_cache, v_cache, seq_lens, scale, *, block_table=None, max_seq_len=None, out=None,
                return_lse=False, lse=None, split_tokens=0, workspace=None, stream=None, window=0):
     """Grouped-query decode attention (MHA at g = h, MQA at g = 1).
@@ -192,19 +216,7 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale, *, block_table=None, max_se
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],):
         raise ValueError("kvattn: seq_lens must be int32 [B]")
     B, h, d = q.shape
-    if block_table is None:
-        if k_cache.shape[0] != B or k_cache.shape[3] != d:
-            raise ValueError("kvattn: contiguous cache must be [B, g, S, d]")
-        g, cache_len, block_size, max_blocks = k_cache.shape[1], k_cache.shape[2], 0, 0
-        default_max = cache_len
-    else:
-        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
-            raise ValueError("kvattn: block_table must be int32 [B, max_blocks]")
-        if k_cache.shape[3] != d:
-            raise ValueError("kvattn: paged cache must be [num_blocks, g, block_size, d]")
-        g, cache_len, block_size, max_blocks = k_cache.shape[1], k_cache.shape[0], k_cache.shape[2], block_table.shape[1]
-        default_max = max_blocks * block_size
-    max_seq_len = default_max if max_seq_len is None else int(max_seq_len)
+    g, cache_len, block_size, max_blocks, max_seq_len = _gqa_geometry(q, k_cache, block_table, max_seq_len)
     if out is None:
         out = torch.empty((B, h, d), dtype=q.dtype, device=q.device)
     elif out.shape != (B, h, d) or out.dtype != q.dtype:
@@ -226,6 +238,48 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale, *, block_table=None, max_se
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
             B, h, g, d, cache_len, block_size, max_blocks, max_seq_len, float(scale), code, int(split_tokens),
             _ptr(ws), nbytes, _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def gqa_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, *, block_table=None, max_seq_len=None,
+                   out=None, return_lse=False, lse=None, split_tokens=0, workspace=None, stream=None, window=0):
+    """Grouped-query decode over an E4M3 KV cache (kvattn_gqa_decode_fp8).
+
+    q [B, h, d] bfloat16; k_cache/v_cache hold E4M3 codes (torch.uint8 or
+    torch.float8_e4m3fn) in the layouts of ``gqa_decode``; k_scale and
+    v_scale are float32 [g], one per KV head (a code c of head j stands for
+    scale[j] * E4M3(c)).  Returns out [B, h, d] bfloat16 (and lse [B, h]).
+    """
+    _need_gpu(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table, out, lse, workspace)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("kvattn: q must be [B, h, d] and the caches 4-d with equal shapes")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("kvattn: the fp8-cache decode takes a bfloat16 query")
+    for c in (k_cache, v_cache):
+        if c.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError("kvattn: fp8 caches must be uint8 or float8_e4m3fn")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],):
+        raise ValueError("kvattn: seq_lens must be int32 [B]")
+    B, h, d = q.shape
+    g, cache_len, block_size, max_blocks, max_seq_len = _gqa_geometry(q, k_cache, block_table, max_seq_len)
+    for sc in (k_scale, v_scale):
+        if sc.dtype != torch.float32 or sc.shape != (g,):
+            raise ValueError("kvattn: k_scale and v_scale must be float32 [num_kv_heads]")
+    if out is None:
+        out = torch.empty((B, h, d), dtype=torch.bfloat16, device=q.device)
+    elif out.shape != (B, h, d) or out.dtype != torch.bfloat16:
+        raise ValueError("kvattn: out must be bfloat16 [B, h, d]")
+    if return_lse and lse is None:
+        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    nbytes = lib.kvattn_gqa_workspace_bytes(B, h, g, d, max_seq_len, block_size, split_tokens, KVATTN_BF16)
+    if nbytes == ctypes.c_size_t(-1).value:
+        nbytes = 0  # the decode call reports the precise problem
+    ws = _workspace(nbytes, workspace, q.device)
+    _check(lib.kvattn_gqa_decode_fp8(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(seq_lens),
+        _ptr(out), _ptr(lse), B, h, g, d, cache_len, block_size, max_blocks, max_seq_len, float(scale), int(window),
+        int(split_tokens), _ptr(ws), nbytes, _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

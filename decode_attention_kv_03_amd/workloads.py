@@ -13,6 +13,13 @@ with ragged lengths ("Compressing the KV Cache ...", KV-Cache Management
 Guardrails), and a DeepSeek-V2-shaped absorbed-MLA layer (128 heads, latent
 512 + RoPE 64, "MQA, GQA, and MLA" section 5).  Values are iid N(0,1) drawn
 in float32 and rounded to the storage dtype (round to nearest even).
+
+An fp8 cache ("Why GQA's KV Cache Savings Don't Fully Reduce TPOT", section
+"When the Serving Engineer Doesn't Get to Choose") is drawn per KV head j
+with a scale s_j = (1 + u_j) / 32, u_j uniform on [0, 1) (separately for K
+and V): the stored codes are torch's E4M3 rounding of N(0,1) / s_j, so the
+cache holds s_j * E4M3(code) ~ N(0,1) and no draw comes near the format's
+largest value (448 * s_j >= 14 standard deviations).
 """
 
 from dataclasses import dataclass, replace
@@ -30,7 +37,7 @@ class GqaWorkload:
     num_kv_heads: int
     head_dim: int
     seq_len: int  # contiguous: every sequence's length and the cache capacity; paged: maximum length
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # cache dtype: "f32", "bf16" or "fp8" (E4M3 codes, bf16 query and output)
     seed: int
     scale: float
     block_size: int = 0  # 0: contiguous cache [B, g, S, d]; else pool [num_blocks, g, block_size, d]
@@ -67,6 +74,8 @@ WORKLOADS = {
         GqaWorkload("llama3_70b_mha_h64_g64_b8_s8192", 8, 64, 64, 128, 8192, "bf16", 31, 1 / math.sqrt(128)),
         GqaWorkload("llama3_70b_gqa_h64_g8_b64_s8192", 64, 64, 8, 128, 8192, "bf16", 32, 1 / math.sqrt(128)),
         GqaWorkload("llama3_70b_mqa_h64_g1_b64_s8192", 64, 64, 1, 128, 8192, "bf16", 33, 1 / math.sqrt(128)),
+        # The 70B GQA-8 layer with an E4M3 cache (one K and one V scale per KV head).
+        GqaWorkload("llama3_70b_gqa_fp8_h64_g8_b64_s8192", 64, 64, 8, 128, 8192, "fp8", 34, 1 / math.sqrt(128)),
         GqaWorkload("paged_gqa_h64_g8_b128_bs16_len1_32768", 128, 64, 8, 128, 32768, "bf16", 4, 1 / math.sqrt(128), 16),
         # Sliding-window decode at Mistral-7B v0.1's shape (h=32, g=8, window 4096) over 32K-token sequences.
         GqaWorkload("mistral7b_swa_h32_g8_b16_s32768_w4096", 16, 32, 8, 128, 32768, "bf16", 6, 1 / math.sqrt(128),
@@ -80,7 +89,23 @@ WORKLOADS = {
 
 
 def torch_dtype(name):
-    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+    """Query/output dtype of a workload (an fp8 cache pairs with a bfloat16 query)."""
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.bfloat16}[name]
+
+
+def _fp8_codes(shape, gen, device, scales, head_dim_axis, chunks=1):
+    """E4M3 codes (uint8) of iid N(0,1) / scales[j], j along ``head_dim_axis``; drawn in ``chunks`` slabs."""
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    view = [1] * len(shape)
+    view[head_dim_axis] = -1
+    inv = (1.0 / scales).reshape(view)
+    n0 = shape[0]
+    step = max(1, (n0 + chunks - 1) // chunks)
+    for a in range(0, n0, step):
+        b = min(n0, a + step)
+        x = torch.randn((b - a, *shape[1:]), generator=gen, device=device, dtype=torch.float32) * inv
+        out[a:b] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    return out
 
 
 def _randn(shape, gen, device, dtype, chunks=1):
@@ -128,19 +153,27 @@ def make_gqa_inputs(w, device="cpu", lens=None, poison_tail=False):
     dt = torch_dtype(w.dtype)
     B, h, g, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
     q = _randn((B, h, d), gen, device, dt)
+    fp8 = w.dtype == "fp8"
+    if fp8:
+        k_scale = (1.0 + torch.rand(g, generator=gen, device=device, dtype=torch.float32)) / 32
+        v_scale = (1.0 + torch.rand(g, generator=gen, device=device, dtype=torch.float32)) / 32
+
+    def cache(shape, chunks, scales):
+        return _fp8_codes(shape, gen, device, scales, 1, chunks) if fp8 else _randn(shape, gen, device, dt, chunks)
+
     if w.paged:
         lens_np, table, N = ragged_lengths_and_table(B, w.seq_len, w.block_size, w.seed)
-        k = _randn((N, g, w.block_size, d), gen, device, dt, chunks=16)
-        v = _randn((N, g, w.block_size, d), gen, device, dt, chunks=16)
+        k = cache((N, g, w.block_size, d), 16, k_scale if fp8 else None)
+        v = cache((N, g, w.block_size, d), 16, v_scale if fp8 else None)
         bt = torch.from_numpy(table).to(device)
     else:
         lens_np = np.full(B, w.seq_len, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
-        k = _randn((B, g, w.seq_len, d), gen, device, dt, chunks=B)
-        v = _randn((B, g, w.seq_len, d), gen, device, dt, chunks=B)
+        k = cache((B, g, w.seq_len, d), B, k_scale if fp8 else None)
+        v = cache((B, g, w.seq_len, d), B, v_scale if fp8 else None)
         bt = None
     if poison_tail:
         _poison(k, v, lens_np, bt, w.block_size)
-    return {
+    inputs = {
         "q": q,
         "k": k,
         "v": v,
@@ -148,6 +181,9 @@ def make_gqa_inputs(w, device="cpu", lens=None, poison_tail=False):
         "block_table": bt,
         "workload": w,
     }
+    if fp8:
+        inputs["k_scale"], inputs["v_scale"] = k_scale, v_scale
+    return inputs
 
 
 def make_mla_inputs(w, device="cpu", lens=None, poison_tail=False):
@@ -176,8 +212,10 @@ def make_mla_inputs(w, device="cpu", lens=None, poison_tail=False):
 
 
 def _poison(k, v, lens_np, bt, block_size):
-    """Fill every cache slot past each sequence's length with NaN (catches reads past the end)."""
-    nan = float("nan")
+    """Fill every cache slot past each sequence's length with NaN (catches reads past the end).
+
+    An fp8 (uint8) cache gets the E4M3 NaN code 0x7F."""
+    nan = float("nan") if k.dtype != torch.uint8 else 0x7F
     for t in (k, v):
         if t is None:
             continue
@@ -200,11 +238,12 @@ def _poison(k, v, lens_np, bt, block_size):
 
 
 def host_view(t):
-    """Host copy in the form the CPU reference takes: float64 for f32, uint16 bit patterns for bf16."""
+    """Host copy in the form the CPU reference takes: float64 for f32, uint16 bit patterns for bf16, raw
+    codes for an fp8 (uint8) cache."""
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype in (torch.int32, torch.int64):
+    if t.dtype in (torch.int32, torch.int64, torch.uint8):
         return t.numpy()
     return t.to(torch.float64).numpy()
 

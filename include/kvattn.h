@@ -144,6 +144,36 @@ kvattn_status kvattn_gqa_decode_window(const void* q, const void* k_cache, const
                                        kvattn_dtype dtype, int32_t split_tokens, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/*
+ * Grouped-query decode over an FP8 KV cache.  Storing the cache in fp8 halves
+ * its bytes, and a GQA cache quantises at the granularity of one KV head
+ * ("Why GQA's KV Cache Savings Don't Fully Reduce TPOT", section "When the
+ * Serving Engineer Doesn't Get to Choose").  The pages name no format or
+ * scale convention; this library reads them as:
+ *
+ *  k_cache,     uint8 codes of the OCP 8-bit float E4M3 ("e4m3fn": bias 7,
+ *  v_cache        3 mantissa bits, subnormals, codes 0x7F/0xFF NaN, largest
+ *                 finite 448), with the shapes and addressing of
+ *                 kvattn_gqa_decode (one byte per element).
+ *  k_scale,     DEVICE fp32 [num_kv_heads]: a K code c of KV head j stands
+ *  v_scale        for k_scale[j] * E4M3(c), a V code for v_scale[j] * E4M3(c).
+ *  q, out       bfloat16, as in kvattn_gqa_decode; lse fp32 or NULL.
+ *
+ * Attention is that of kvattn_gqa_decode_window over the dequantised cache
+ * (window 0: every token).  Codes are widened exactly to bfloat16 and the
+ * scales are applied in fp32 (k_scale[j] to the softmax scale, v_scale[j] to
+ * the output), so results match a dequantise-then-attend reference to fp32
+ * accumulation order.  Supported: head_dim == 128, h/g <= 128.  The workspace
+ * kvattn_gqa_workspace_bytes reports for the same arguments (any dtype) is
+ * enough.  NULL scales are KVATTN_ERR_INVALID.
+ */
+kvattn_status kvattn_gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                    const float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                    void* out, float* lse, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int64_t cache_len, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int32_t max_seq_len, float scale, int32_t window,
+                                    int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes kvattn_gqa_decode needs for these arguments (0 when no split is needed).
  * block_size is 0 for a contiguous cache (block_table == NULL) and the pool's block size for a
  * paged one: the split planner treats the two differently.  Returns (size_t)-1 for arguments
@@ -194,7 +224,7 @@ int32_t kvattn_mla_split_tokens(int32_t batch, int32_t num_heads, int32_t max_se
                                 int32_t block_size, int32_t split_tokens);
 
 /*
- * Measurement utility: the next kvattn_gqa_decode or kvattn_mla_decode call
+ * Measurement utility: the next decode call (any kvattn_*_decode* entry point)
  * made on the calling thread records `start_event` when its split-K kernel
  * (the kernel that reads the cache) starts executing and `stop_event` when it
  * ends, so the caller can time that kernel alone with hipEventElapsedTime.

@@ -9,8 +9,10 @@ from decode_attention_kv_03_amd import workloads as W
 def test_named_workloads_have_expected_shapes():
     c = W.WORKLOADS
     assert c["gqa_h8_g2_d128_s512_b1_f32"].dtype == "f32"
-    w70 = [c[n] for n in c if n.startswith("llama3_70b")]
+    w70 = [c[n] for n in c if n.startswith("llama3_70b") and c[n].dtype == "bf16"]
     assert sorted((w.num_kv_heads, w.batch) for w in w70) == [(1, 64), (8, 64), (64, 8)]
+    f8 = c["llama3_70b_gqa_fp8_h64_g8_b64_s8192"]
+    assert (f8.dtype, f8.num_q_heads, f8.num_kv_heads, f8.batch, f8.seq_len) == ("fp8", 64, 8, 64, 8192)
     m = c["deepseek_v2_mla_h128_b32_s8192"]
     assert (m.num_heads, m.d_latent + m.d_rope, m.batch, m.seq_len) == (128, 576, 32, 8192)
     assert abs(m.scale - 1 / np.sqrt(192)) < 1e-12
@@ -53,3 +55,16 @@ def test_host_view_round_trips_bits():
     h = W.host_view(t)
     assert h.dtype == np.uint16
     assert torch.equal(torch.from_numpy(h.view(np.int16)).view(torch.bfloat16), t)
+
+
+def test_fp8_inputs_hold_codes_and_per_head_scales():
+    w = W.GqaWorkload("f8", 2, 8, 2, 128, 300, "fp8", 11, 0.1)
+    x = W.make_gqa_inputs(w, "cpu", lens=[300, 17], poison_tail=True)
+    assert x["q"].dtype == torch.bfloat16 and x["k"].dtype == torch.uint8 and x["k_scale"].shape == (2,)
+    assert torch.all((x["k_scale"] >= 1 / 32) & (x["k_scale"] < 2 / 32))
+    # codes past each length are the E4M3 NaN code; none inside (no draw saturates)
+    assert torch.all(x["k"][1, :, 17:] == 0x7F) and not torch.any(x["k"][0] == 0x7F)
+    vals = x["v"][0].view(torch.float8_e4m3fn).float() * x["v_scale"][:, None, None]
+    assert abs(float(vals.std()) - 1.0) < 0.05
+    y = W.make_gqa_inputs(w, "cpu", lens=[300, 17], poison_tail=True)
+    assert torch.equal(x["k"], y["k"]) and torch.equal(x["v_scale"], y["v_scale"])
