@@ -60,12 +60,14 @@ def algorithmic(w, lens):
         lens = np.minimum(lens, w.window)  # a sliding window reads only its last `window` tokens
     ntok = int(np.sum(lens))
     if hasattr(w, "num_kv_heads"):
-        eb = 4 if w.dtype == "f32" else 2
+        eb = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]  # cache bytes per element
+        qb = 4 if w.dtype == "f32" else 2  # query/output bytes per element (bf16 beside an fp8 cache)
         kv = 2 * w.num_kv_heads * w.head_dim * eb * ntok
-        qo = 2 * w.batch * w.num_q_heads * w.head_dim * eb
+        qo = 2 * w.batch * w.num_q_heads * w.head_dim * qb
+        scales = 2 * 4 * w.num_kv_heads if w.dtype == "fp8" else 0
         table = 4 * int(np.sum((lens + w.block_size - 1) // w.block_size)) if w.paged else 0
         flops = 4 * w.num_q_heads * w.head_dim * ntok
-        return kv + qo + table, flops
+        return kv + qo + scales + table, flops
     width = w.d_latent + w.d_rope
     kv = width * 2 * ntok
     qo = w.batch * w.num_heads * (width + w.d_latent) * 2
@@ -84,7 +86,10 @@ def cpu_baseline(w, x, seconds):
 
     lens = W.host_view(x["seq_lens"])
     bf16 = w.dtype == "bf16"
+    fp8 = w.dtype == "fp8"
     q = W.host_view(x["q"])
+    if fp8:
+        k_scale, v_scale = W.host_view(x["k_scale"]), W.host_view(x["v_scale"])
     order = [int(b) for b in np.random.default_rng(0).permutation(w.batch)]
     host = {}  # host copies of the sampled sequences' inputs, made once (not timed)
 
@@ -117,7 +122,14 @@ def cpu_baseline(w, x, seconds):
         i += 1
         args = inputs(b)
         t0 = time.perf_counter()
-        if hasattr(w, "num_kv_heads"):
+        if fp8:
+            if w.paged:
+                oracle.paged_gqa_decode_fp8(q[b:b + 1], args[0], args[1], k_scale, v_scale, args[2], lens[b:b + 1],
+                                            w.block_size, w.scale, window=w.window)
+            else:
+                oracle.gqa_decode_fp8(q[b:b + 1], args[0], args[1], k_scale, v_scale, lens[b:b + 1], w.scale,
+                                      window=w.window)
+        elif hasattr(w, "num_kv_heads"):
             if w.paged:
                 oracle.paged_gqa_decode(q[b:b + 1], args[0], args[1], args[2], lens[b:b + 1], w.block_size, w.scale,
                                         bf16=bf16, window=w.window)
@@ -138,7 +150,8 @@ def cpu_baseline(w, x, seconds):
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"{done} single-sequence oracle calls ({distinct} distinct of the {w.batch} sequences of {w.name}, "
-                  f"cycled), fp64 NumPy, bf16->fp64 widening included, {t_total:.1f} s of CPU time",
+                  f"cycled), fp64 NumPy, {'E4M3 decoding' if fp8 else 'bf16->fp64 widening'} included, "
+                  f"{t_total:.1f} s of CPU time",
     }
 
 
@@ -179,7 +192,8 @@ def main():
     import numpy as np
     import torch
 
-    from decode_attention_kv_03_amd import gqa_decode, mla_decode, gqa_workspace_bytes, mla_workspace_bytes
+    from decode_attention_kv_03_amd import (gqa_decode, gqa_decode_fp8, gqa_workspace_bytes, mla_decode,
+                                            mla_workspace_bytes)
     from decode_attention_kv_03_amd import time_next_kernel
     from decode_attention_kv_03_amd.profiling import lookup_traffic
     from decode_attention_kv_03_amd import workloads as W
@@ -230,7 +244,11 @@ def main():
 
     def step(i):
         x = xs[i % copies]
-        if is_gqa:
+        if is_gqa and w.dtype == "fp8":
+            gqa_decode_fp8(x["q"], x["k"], x["v"], x["k_scale"], x["v_scale"], x["seq_lens"], w.scale,
+                           block_table=x["block_table"], max_seq_len=max_len, out=out, split_tokens=args.split_tokens,
+                           workspace=ws, stream=stream, window=w.window)
+        elif is_gqa:
             gqa_decode(x["q"], x["k"], x["v"], x["seq_lens"], w.scale, block_table=x["block_table"],
                        max_seq_len=max_len, out=out, split_tokens=args.split_tokens, workspace=ws, stream=stream,
                        window=w.window)
@@ -285,7 +303,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
         "traffic": (traffic["fetch_bytes"] + traffic["write_bytes"]) if traffic else None,
-        "kernel": ("gqa_split_bf16" if w.dtype == "bf16" else "gqa_split_f32") if is_gqa else "mla_split_bf16",
+        "kernel": f"gqa_split_{w.dtype}" if is_gqa else "mla_split_bf16",
         "kernel_us_mean": round(mean_kern_s * 1e6, 2),
         "kernel_us_p10_p50_p90": [round(float(np.percentile(kern_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
         "algorithmic_bytes_per_launch": int(nbytes),
@@ -326,8 +344,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded iid N(0,1), rounded to the storage dtype)",
+        "dtype": "fp8_e4m3 cache, bf16 matrix cores, fp32 accumulation" if w.dtype == "fp8" else w.dtype,
+        "data": ("synthetic (seeded iid N(0,1) over per-KV-head scales (1+U[0,1))/32, rounded to E4M3; bf16 query)"
+                 if w.dtype == "fp8" else "synthetic (seeded iid N(0,1), rounded to the storage dtype)"),
         "config": cfg,
         "roofline": roofline,
         "cpu_baseline": cpu,
