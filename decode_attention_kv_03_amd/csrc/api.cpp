@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <string>
@@ -69,17 +70,44 @@ int32_t plan_gqa_split(int32_t batch, int32_t h, int32_t g, int32_t max_seq_len,
   return (int32_t)std::min(chunk, round_up(S, KVATTN_SPLIT_ALIGN));
 }
 
-// Tokens per split for MLA: one 128-head workgroup fills a CU, so aim for
-// one workgroup per CU.
-int32_t plan_mla_split(int32_t batch, int32_t h, int32_t max_seq_len, int32_t requested) {
-  (void)h;
+// MLA work plan.  The decode kernel's workgroups take pieces of the
+// sequences, cut on the device from the actual lengths (mla_plan.hip): the
+// shortest piece length (a multiple of 32, at least kMlaMinChunk) that gives
+// at most max(kCUs, batch) pieces (one 128-head workgroup fills a CU), or the
+// caller's split_tokens.  The host only bounds the number of pieces.
+constexpr int32_t kMlaMinChunk = 256;
+
+// Piece length the plan chooses when every sequence holds max_seq_len tokens.
+int32_t plan_mla_split(int32_t batch, int32_t max_seq_len, int32_t requested) {
   if (requested > 0) return requested;
-  const int64_t S = max_seq_len > 0 ? max_seq_len : 1;
-  int64_t chunk = round_up((S * batch + kCUs - 1) / kCUs, KVATTN_SPLIT_ALIGN);
-  chunk = std::max<int64_t>(chunk, 256);
-  chunk = std::min<int64_t>(chunk, 4096);
-  chunk = std::min(chunk, round_up(S, KVATTN_SPLIT_ALIGN));
-  return (int32_t)chunk;
+  const int64_t S = std::max<int32_t>(max_seq_len, 1);
+  const int64_t per_seq = std::max<int64_t>(kCUs, batch) / batch;  // pieces each sequence may take
+  const int64_t t = round_up((S + per_seq - 1) / per_seq, 32);
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(t, kMlaMinChunk), INT32_MAX);
+}
+
+// Upper bound on the number of pieces, or -1 if it overflows.
+int64_t mla_max_pieces(int32_t batch, int32_t max_seq_len, int32_t requested) {
+  const int64_t S = std::max<int32_t>(max_seq_len, 1);
+  const int64_t n = requested > 0 ? (int64_t)batch * ((S + requested - 1) / requested)
+                                  : std::max<int64_t>(kCUs, batch);
+  return n > (int64_t)INT32_MAX / 8 ? -1 : n;
+}
+
+// Workspace regions of an MLA call: partial outputs, partial log-sum-exps, the plan's pieces,
+// per-sequence piece ranges and the plan's counts, each 256-byte aligned.
+struct MlaWorkspace {
+  size_t part_o, part_lse, pieces, seq_pieces, plan_count, total;
+};
+MlaWorkspace mla_workspace(int64_t batch, int64_t heads, int64_t max_pieces, int64_t d_c) {
+  MlaWorkspace w{};
+  w.part_o = 0;
+  w.part_lse = w.part_o + (size_t)round_up(max_pieces * heads * d_c * (int64_t)sizeof(float), 256);
+  w.pieces = w.part_lse + (size_t)round_up(max_pieces * heads * (int64_t)sizeof(float), 256);
+  w.seq_pieces = w.pieces + (size_t)round_up(max_pieces * 16, 256);
+  w.plan_count = w.seq_pieces + (size_t)round_up(batch * 8, 256);
+  w.total = w.plan_count + 256;
+  return w;
 }
 
 int32_t n_splits(int32_t max_seq_len, int32_t split) {
@@ -275,7 +303,7 @@ int32_t kvattn_mla_split_tokens(int32_t batch, int32_t h, int32_t max_seq_len, i
                                 int32_t split_tokens) {
   (void)block_size;
   if (batch < 1 || h < 1 || split_tokens < 0) return -1;
-  return plan_mla_split(batch, h, max_seq_len, split_tokens);
+  return plan_mla_split(batch, max_seq_len, split_tokens);
 }
 
 size_t kvattn_gqa_workspace_bytes(int32_t batch, int32_t h, int32_t g, int32_t d, int32_t max_seq_len,
@@ -292,10 +320,12 @@ size_t kvattn_mla_workspace_bytes(int32_t batch, int32_t h, int32_t d_c, int32_t
                                   int32_t block_size, int32_t split_tokens, kvattn_dtype dtype) {
   (void)dtype;
   (void)d_r;
+  (void)block_size;
   if (batch < 1 || h < 1 || d_c < 1 || max_seq_len < 0 || split_tokens < 0 || split_tokens % KVATTN_SPLIT_ALIGN != 0)
     return (size_t)-1;
-  const int32_t split = plan_mla_split(batch, h, max_seq_len, split_tokens);
-  return partial_bytes(batch, h, n_splits(max_seq_len, split), d_c);
+  const int64_t max_pieces = mla_max_pieces(batch, max_seq_len, split_tokens);
+  if (max_pieces < 0) return (size_t)-1;
+  return mla_workspace(batch, h, max_pieces, d_c).total;
 }
 
 kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
@@ -355,12 +385,26 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
     return st;
   if ((st = check_split(split_tokens)) != KVATTN_OK) return st;
 
-  const int32_t split = plan_mla_split(batch, num_heads, max_seq_len, split_tokens);
-  const int32_t nsplit = n_splits(max_seq_len, split);
-  const size_t need = partial_bytes(batch, num_heads, nsplit, d_latent);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
+  const int64_t max_pieces = mla_max_pieces(batch, max_seq_len, split_tokens);
+  if (max_pieces < 0)
+    return fail(KVATTN_ERR_UNSUPPORTED, "batch %lld x max_seq_len %lld needs too many pieces for this split_tokens",
+                batch, max_seq_len);
+  const MlaWorkspace wl = mla_workspace(batch, num_heads, max_pieces, d_latent);
+  if (workspace == nullptr || workspace_bytes < wl.total)
+    return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)wl.total,
                 workspace == nullptr ? 0 : (long long)workspace_bytes);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+
+  kvattn::MlaPlanArgs pa{};
+  pa.seq_lens = seq_lens;
+  pa.batch = batch;
+  pa.len_cap = max_seq_len;
+  pa.work_items = kCUs;
+  pa.min_chunk = kMlaMinChunk;
+  pa.fixed_chunk = split_tokens;
+  pa.pieces = reinterpret_cast<int4*>(ws + wl.pieces);
+  pa.seq_pieces = reinterpret_cast<int2*>(ws + wl.seq_pieces);
+  pa.plan_count = reinterpret_cast<int32_t*>(ws + wl.plan_count);
 
   kvattn::DecodeArgs a{};
   a.q = q;
@@ -379,20 +423,20 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
   a.block_shift = paged ? pow2_shift(block_size) : -1;
   a.max_blocks = paged ? max_blocks_per_seq : 0;
   a.len_cap = max_seq_len;
-  a.split_tokens = split;
-  a.n_split = nsplit;
   a.scale_log2 = scale * kvattn::kLog2eHost;
-  if (nsplit > 1) {
-    a.part_o = static_cast<float*>(workspace);
-    a.part_lse = a.part_o + (int64_t)batch * num_heads * nsplit * d_latent;
-  }
+  a.part_o = reinterpret_cast<float*>(ws + wl.part_o);
+  a.part_lse = reinterpret_cast<float*>(ws + wl.part_lse);
+  a.pieces = pa.pieces;
+  a.seq_pieces = pa.seq_pieces;
+  a.plan_count = pa.plan_count;
+  a.max_pieces = (int32_t)max_pieces;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = kvattn::launch_mla_bf16(a, s, ev);
+  hipError_t e = kvattn::launch_mla_plan(pa, s);
+  if (e != hipSuccess) return hip_status(e, "MLA plan kernel launch");
+  e = kvattn::launch_mla_bf16(a, s, ev);
   if (e != hipSuccess) return hip_status(e, "MLA kernel launch");
-  if (nsplit > 1) {
-    e = kvattn::launch_merge(a, d_latent, true, s);
-    if (e != hipSuccess) return hip_status(e, "merge kernel launch");
-  }
+  e = kvattn::launch_mla_merge_pieces(a, s);
+  if (e != hipSuccess) return hip_status(e, "merge kernel launch");
   return ok();
 }
 

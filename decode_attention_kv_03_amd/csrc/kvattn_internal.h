@@ -48,6 +48,27 @@ struct DecodeArgs {
   int32_t n_split;          // splits per sequence in the grid
   float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
   int32_t ring_depth;       // bf16 GQA: LDS ring stages (2 or 3)
+  // MLA work plan, written on the device by the plan kernel:
+  //   pieces[q] = (sequence, first token, end token, 1 if it is the sequence's only piece)
+  //   seq_pieces[b] = (first piece, number of pieces); plan_count = {pieces, piece length}
+  // Partials of piece q, head i: part_o[(q * h + i) * d_v], part_lse[q * h + i].
+  const int4* pieces;
+  const int2* seq_pieces;
+  const int32_t* plan_count;
+  int32_t max_pieces;       // grid bound: the plan never makes more pieces
+};
+
+// Arguments of the MLA plan kernel.
+struct MlaPlanArgs {
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t len_cap;
+  int32_t work_items;       // target number of pieces when the piece length is chosen
+  int32_t min_chunk;        // shortest chosen piece length
+  int32_t fixed_chunk;      // > 0: use this piece length instead
+  int4* pieces;
+  int2* seq_pieces;
+  int32_t* plan_count;
 };
 
 // Optional events recorded when a launch's kernel starts and ends (null: none).
@@ -60,6 +81,8 @@ hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream, const LaunchE
 hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_gqa_fp8(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
+hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t stream);
+hipError_t launch_mla_merge_pieces(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_hbm_read_probe(const void* buf, int64_t n16, uint32_t* sink, int workgroups, hipStream_t stream);
 // Log-sum-exp merge of the per-split partials into out/lse; d_v = 128 or 512.
 hipError_t launch_merge(const DecodeArgs& a, int d_v, bool out_bf16, hipStream_t stream);

@@ -13,8 +13,8 @@
 // (the 16x16x32 shape issues at well under half of it):
 //   S^T[32 tok x 32 heads] = C_tile[32 x 576] * Q^T[576 x 32]
 //   O^T[32 cols x 32 heads] += C_tile[:, cols]^T * P^T[32 tok x 32 heads]
-// A workgroup (8 waves, two per SIMD) owns one (sequence, split) and all
-// heads.  Waves pair up per 32-head block: each wave of a pair holds the
+// A workgroup (8 waves, two per SIMD) owns one piece of a sequence (a run
+// of its tokens, from the device-side plan in mla_plan.hip) and all heads.  Waves pair up per 32-head block: each wave of a pair holds the
 // query for half of the 576 dims (18 reduction steps of 16) and the output
 // accumulators for half of the 512 latent columns (8 blocks of 32), which
 // keeps both under the 256 registers a wave has at two waves per SIMD.  The
@@ -93,24 +93,28 @@ __device__ __forceinline__ int slot_of(const DecodeArgs& a, int t) {
 }
 
 __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
-  // 1-D grid, XCD-aware: workgroup w runs on XCD w % 8, and every split of
-  // sequence b gets an id with the same residue, so a sequence's queries and
-  // partials stay in one XCD's L2.
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int split = slot % a.n_split;
-  const int b = (slot / a.n_split) * 8 + xcd;
-  if (b >= a.batch) return;
+  // One workgroup per piece of the device-side plan.  1-D grid, XCD-aware:
+  // workgroup w runs on XCD w % 8, and XCD x takes the x-th eighth of the
+  // pieces, a run of consecutive pieces (so about an eighth of all tokens,
+  // and most of a sequence's pieces on one XCD, whose L2 then serves its
+  // queries).
+  const int n_pieces = a.plan_count[0];
+  const int per_xcd = (n_pieces + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  const int piece = (blockIdx.x & 7) * per_xcd + slot;
+  if (slot >= per_xcd || piece >= n_pieces) return;
+  const int4 pc = a.pieces[piece];
+  const int b = pc.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps wave-derived values in SGPRs
   const int pair = wave >> 1, half = wave & 1;
   const int c32 = lane & 31, g = lane >> 5;
   const int h = a.num_q_heads;
 
-  const int len = clamp_len(a.seq_lens[b], a.len_cap);
-  const int t_begin = split * a.split_tokens;
-  const bool final_out = (a.n_split == 1);
-  if (!final_out && t_begin >= len) return;
-  const int t_end = min(len, t_begin + a.split_tokens);
+  // The piece's tokens (t_begin a multiple of the tile), and whether it is
+  // its sequence's only piece (then the output is final).
+  const int t_begin = pc.y, t_end = pc.z;
+  const bool final_out = pc.w != 0;
 
   __shared__ __attribute__((aligned(1024))) unsigned char tiles[kNBuf][kTileBytes];
   __shared__ __attribute__((aligned(16))) float sx[kSxFloats];
@@ -155,8 +159,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   // Fast copies need each 16-row half of the tile to be one run of
   // consecutive cache rows: always true for a contiguous cache, and for a
   // paged one whose block size is a multiple of 16 (tiles start at
-  // multiples of 32 tokens).  The ragged last tile of a split takes the
-  // general path, which clamps every row into the split.
+  // multiples of 32 tokens).  The ragged last tile of a piece takes the
+  // general path, which clamps every row into the piece.
   const bool halves_contiguous = a.block_size == 0 || (a.block_size & 15) == 0;
   auto issue_tile = [&](int t0, int buf) __attribute__((always_inline)) {
     const uint32_t dst = (uint32_t)(uintptr_t)&tiles[buf][0];
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 
   // One tile: wait for its copies, issue the copies of tile it+2, scores,
   // partial-score swap, softmax, value product.  kLast marks the last tile
-  // of the split, the only one that can be ragged; the others are compiled
+  // of the piece, the only one that can be ragged; the others are compiled
   // without any masking.
   auto tile_step = [&](int it, auto last_tag) __attribute__((always_inline)) {
     constexpr bool kLast = decltype(last_tag)::value;
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
     // Online softmax on c * score (c = scale * log2 e, log2 units); P^T is
     // packed straight into the B-operand layout.  The tile maximum of c * s
     // is c times the raw maximum (the minimum, for a negative scale).  Only
-    // the last tile of a split can hold tokens past its end; its masked
+    // the last tile of a piece can hold tokens past its end; its masked
     // scores are set to the neutral element of that extremum and their
     // probabilities to zero.
     const float c = a.scale_log2;
@@ -397,14 +401,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
       }
     if (a.lse != nullptr && g == 0 && half == 0) a.lse[row] = lse2 * kLn2;
   } else {
-    float* po = a.part_o + (row * a.n_split + split) * kMlaLatent + 4 * g;
+    const int64_t prow = (int64_t)piece * h + head;
+    float* po = a.part_o + prow * kMlaLatent + 4 * g;
 #pragma unroll
     for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4*>(po + 32 * (2 * i + half) + 8 * q) =
             f32x4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]} * inv;
-    if (g == 0 && half == 0) a.part_lse[row * a.n_split + split] = lse2;
+    if (g == 0 && half == 0) a.part_lse[prow] = lse2;
   }
 }
 
@@ -412,8 +417,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 
 hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
   if (a.num_q_heads % 16 != 0 || a.num_q_heads > kMaxMlaHeads) return hipErrorInvalidValue;
-  const int seq_groups = (a.batch + 7) / 8;
-  const dim3 grid(8 * seq_groups * a.n_split);
+  const dim3 grid(8 * ((a.max_pieces + 7) / 8));
   hipExtLaunchKernelGGL(mla_split_bf16, grid, dim3(kWaves * 64), 0, stream, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }

@@ -1,0 +1,175 @@
+// Device-side work plan for MLA decode, and the merge of its pieces.
+//
+// An MLA split writes a partial as large as the output rows of all heads
+// (128 heads x 513 fp32 for DeepSeek-V2, against 1152 cache bytes per
+// token), so splits must stay long, and one 128-head workgroup fills a
+// compute unit.  With ragged sequence lengths, fixed-size splits then leave
+// either a few long workgroups that set the pace or a second round of
+// workgroups.  The plan instead looks at the actual lengths (they live in
+// device memory, so the plan is made on the device, by one wave, in the
+// stream of the kernels that use it) and picks the shortest piece length t
+// (a multiple of 32, at least min_chunk) for which the sequences, each cut
+// into ceil(len / t) pieces, give at most max(work_items, batch) pieces: one
+// round of workgroups with the longest piece as short as that allows.  A
+// sequence's pieces are equal in length up to the 32-token tile (its cuts
+// sit on multiples of 32), so a piece is a (sequence, first token, end
+// token) triple and the pieces of a sequence are consecutive.  A caller's
+// split_tokens fixes t instead.  A sequence covered by one piece gets its
+// output written directly by the decode kernel; the others are combined by
+// the log-sum-exp merge below.
+#include "device_common.h"
+#include "kvattn_internal.h"
+
+namespace kvattn {
+namespace {
+
+// The plan runs as one wave: lane l handles sequences l, l+64, ...; the
+// lengths of the first kCached rounds stay in registers across the search.
+constexpr int kCached = 8;
+
+__device__ __forceinline__ int64_t align32(int64_t x) { return (x + 31) & ~int64_t(31); }
+
+// Length of each piece of a sequence of `len` tokens cut for piece length t:
+// ceil(len / t) pieces of equal length, rounded up to the tile.
+__device__ __forceinline__ int64_t piece_len(int64_t len, int64_t t) {
+  const int64_t n = (len + t - 1) / t;
+  return align32((len + n - 1) / n);
+}
+
+// Pieces of a sequence of `len` tokens for piece length t (an empty sequence
+// keeps one empty piece).
+__device__ __forceinline__ int64_t pieces_of(int64_t len, int64_t t) {
+  return len > 0 ? (len + t - 1) / t : 1;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan_int(int v) {
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
+  const int lane = threadIdx.x;
+  int cl[kCached];
+#pragma unroll
+  for (int i = 0; i < kCached; ++i) {
+    const int b = lane + 64 * i;
+    cl[i] = b < p.batch ? clamp_len(p.seq_lens[b], p.len_cap) : -1;  // -1: no sequence
+  }
+  // Number of pieces for piece length t, saturated at cap + 1 (enough to compare with cap).
+  auto pieces_for = [&](int64_t t, int64_t cap) {
+    int64_t n = 0;
+#pragma unroll
+    for (int i = 0; i < kCached; ++i)
+      if (cl[i] >= 0) n += pieces_of(cl[i], t);
+    for (int b = lane + 64 * kCached; b < p.batch && n <= cap; b += 64) n += pieces_of(clamp_len(p.seq_lens[b], p.len_cap), t);
+    return wave_sum_int((int)(n < cap + 1 ? n : cap + 1));
+  };
+  int64_t t = p.fixed_chunk;
+  if (t <= 0) {
+    // Shortest multiple of 32 in [min_chunk, len_cap rounded up] with at most
+    // cap pieces (the count only falls as t grows, and the upper end gives
+    // one piece per sequence).
+    const int64_t cap = p.work_items > p.batch ? p.work_items : p.batch;
+    int64_t lo = p.min_chunk / 32, hi = align32(p.len_cap > p.min_chunk ? p.len_cap : p.min_chunk) / 32;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (pieces_for(32 * mid, cap) <= cap) hi = mid;
+      else lo = mid + 1;
+    }
+    t = 32 * lo;
+  }
+
+  // Sequences in rounds of 64; the first piece of each is an exclusive
+  // prefix sum carried across rounds.
+  int carry = 0;
+  for (int base = 0, i = 0; base < p.batch; base += 64, ++i) {
+    const int b = base + lane;
+    int len = -1;
+#pragma unroll
+    for (int k = 0; k < kCached; ++k)
+      if (k == i) len = cl[k];
+    if (i >= kCached && b < p.batch) len = clamp_len(p.seq_lens[b], p.len_cap);
+    const int count = b < p.batch ? (int)pieces_of(len, t) : 0;
+    const int incl = wave_scan_int(count);
+    const int first = carry + incl - count;
+    if (b < p.batch) {
+      p.seq_pieces[b] = make_int2(first, count);
+      const int64_t plen = len > 0 ? piece_len(len, t) : 0;
+      for (int j = 0; j < count; ++j) {
+        const int64_t lo = j * plen;
+        const int64_t hi = lo + plen < len ? lo + plen : len;
+        p.pieces[first + j] = make_int4(b, (int)lo, (int)hi, count == 1 ? 1 : 0);
+      }
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) {
+    p.plan_count[0] = carry;
+    p.plan_count[1] = (int)t;
+  }
+}
+
+// Log-sum-exp merge of the pieces of each sequence with more than one.
+// Piece q leaves o_q (normalised over its own tokens) and lse_q (log2 of its
+// normaliser); M = max lse_q, w_q = 2^(lse_q - M), o = sum w_q o_q / sum w_q,
+// lse = M + log2 sum w_q.  One wave per (sequence, head); lane l owns
+// output columns 4l .. 4l+3 and 4(l+64) .. 4(l+64)+3.
+__global__ __launch_bounds__(64) void mla_merge_pieces(DecodeArgs a) {
+  const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int2 sp = a.seq_pieces[b];
+  if (sp.y <= 1) return;  // written directly by the decode kernel
+  const int h = a.num_q_heads;
+  const int64_t row = (int64_t)b * h + head;
+
+  float M = -INFINITY;
+  for (int s = lane; s < sp.y; s += 64) M = fmaxf(M, a.part_lse[(int64_t)(sp.x + s) * h + head]);
+  M = wave_reduce_max(M);
+  float L = 0.f;
+  if (M != -INFINITY)
+    for (int s = lane; s < sp.y; s += 64) L += fast_exp2(a.part_lse[(int64_t)(sp.x + s) * h + head] - M);
+  L = wave_reduce_sum(L);
+  const bool empty = !(L > 0.f);
+  const float inv = empty ? 0.f : 1.f / L;
+
+  for (int d4 = lane; d4 < kMlaLatent / 4; d4 += 64) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (!empty) {
+      for (int s = 0; s < sp.y; ++s) {
+        const int64_t pr = (int64_t)(sp.x + s) * h + head;
+        const float w = fast_exp2(a.part_lse[pr] - M);
+        acc += w * *reinterpret_cast<const f32x4*>(a.part_o + pr * kMlaLatent + 4 * d4);
+      }
+    }
+    acc *= inv;
+    uint16_t* o = static_cast<uint16_t*>(a.out) + row * kMlaLatent + 4 * d4;
+    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+  }
+  if (lane == 0 && a.lse != nullptr) a.lse[row] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t stream) {
+  mla_plan<<<1, 64, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_merge_pieces(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_q_heads, a.batch);
+  mla_merge_pieces<<<grid, 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace kvattn

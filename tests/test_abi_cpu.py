@@ -125,14 +125,28 @@ def test_split_planner():
     assert f(8, 64, 64, 8192, 0, 0) == 8192
     assert f(128, 64, 8, 32768, 16, 0) == 2048    # paged
     m = lib.kvattn_mla_split_tokens
-    assert m(32, 128, 8192, 0, 0) == 1024
+    assert m(32, 128, 8192, 0, 0) == 1024     # 32 x 8192 tokens over 256 compute units
+    assert m(32, 128, 16384, 64, 0) == 2048
+    assert m(1, 128, 1000, 0, 0) == 256       # shortest chosen piece
     assert m(32, 128, 8192, 0, 512) == 512
 
 
+def _mla_workspace(batch, heads, pieces, d_c=512):
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    return up(pieces * heads * d_c * 4) + up(pieces * heads * 4) + up(pieces * 16) + up(batch * 8) + 256
+
+
 def test_mla_workspace_bytes():
-    # 8 splits of fp32 partial outputs (512 wide) and log-sum-exps per (sequence, head)
-    assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 8192, 0, 0, K.KVATTN_BF16) == 32 * 128 * 8 * 513 * 4
-    assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 1024, 0, 1024, K.KVATTN_BF16) == 0  # one split
+    # pieces of the device-side plan: at most max(256, batch) (one per compute unit, or per sequence),
+    # each with fp32 partial outputs (512 wide) and log-sum-exps for every head, plus the plan itself
+    assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 8192, 0, 0, K.KVATTN_BF16) == _mla_workspace(32, 128, 256)
+    assert lib.kvattn_mla_workspace_bytes(300, 128, 512, 64, 64, 0, 0, K.KVATTN_BF16) == _mla_workspace(300, 128, 300)
+    # a requested piece length bounds the pieces by ceil(max_seq_len / split) per sequence
+    assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 1024, 0, 1024, K.KVATTN_BF16) == _mla_workspace(32, 128, 32)
+    assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 1025, 0, 1024, K.KVATTN_BF16) == _mla_workspace(32, 128, 64)
+    assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 1024, 0, 100, K.KVATTN_BF16) == ctypes.c_size_t(-1).value
 
 
 @pytest.mark.parametrize(
@@ -150,6 +164,7 @@ def test_mla_workspace_bytes():
         (dict(split=32), K.KVATTN_ERR_INVALID),
         (dict(bt=P, bs=0, maxb=4), K.KVATTN_ERR_INVALID),
         (dict(cache_len=8192, maxlen=8192, split=256), K.KVATTN_ERR_WORKSPACE),
+        (dict(), K.KVATTN_ERR_WORKSPACE),  # the plan always needs a workspace
     ],
 )
 def test_mla_rejects_bad_arguments_before_touching_the_gpu(kw, status):

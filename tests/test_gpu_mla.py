@@ -91,6 +91,38 @@ def test_zero_lengths():
         assert_close(o[1:2], ref)
 
 
+@pytest.mark.parametrize("B,lens_seed,max_len,split,bs", [
+    (5, 0, 2600, 0, 0),       # few tokens in all: shortest pieces, cuts away from sequence starts
+    (300, 1, 120, 0, 0),      # more sequences than the plan kernel's threads (two scan rounds)
+    (300, 2, 90, 64, 16),     # ... paged, requested piece length
+    (40, 3, 3000, 0, 32),     # paged ragged batch, pieces spanning sequence boundaries
+    (7, 4, 5000, 320, 0),     # requested piece length that is not a power of two
+])
+def test_device_plan_ragged_batches(B, lens_seed, max_len, split, bs):
+    """The device-side piece plan on ragged batches: empty, one-token and multi-piece sequences."""
+    rng = np.random.default_rng(lens_seed)
+    lens = rng.integers(0, max_len + 1, size=B)
+    lens[rng.integers(0, B)] = 0
+    lens[rng.integers(0, B)] = 1
+    h = 16
+    if bs:
+        w = W.MlaWorkload(f"mla_plan_paged_{B}", B, h, max_len, 900 + lens_seed, 1 / np.sqrt(192), block_size=bs)
+        note(f"mla plan B={B} max_len={max_len} split={split} block_size={bs}")
+        x = W.make_mla_inputs(w, DEV, poison_tail=True)
+    else:
+        w = W.MlaWorkload(f"mla_plan_{B}", B, h, max_len, 900 + lens_seed, 1 / np.sqrt(192))
+        note(f"mla plan B={B} max_len={max_len} split={split} lens sum={int(lens.sum())}")
+        x = W.make_mla_inputs(w, DEV, lens=lens, poison_tail=True)
+    ref, ref_lse = reference(x)
+    out, lse = run(x, split_tokens=split)
+    assert_close(out.float().cpu().numpy(), ref, "plan")
+    l_ref = np.where(np.isneginf(ref_lse), -np.inf, ref_lse)
+    got = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(got), np.isneginf(l_ref))
+    fin = np.isfinite(l_ref)
+    np.testing.assert_allclose(got[fin], l_ref[fin], atol=2e-3, rtol=1e-4)
+
+
 @pytest.mark.parametrize("bs", [16, 5, 64])
 def test_paged(bs):
     w = W.MlaWorkload(f"mla_paged_bs{bs}", 4, 128, 400, 40 + bs, 1 / np.sqrt(192), block_size=bs)
