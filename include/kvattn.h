@@ -57,8 +57,9 @@
  *    split_tokens = 0 lets the library choose; otherwise it must be a
  *    positive multiple of KVATTN_SPLIT_ALIGN.  Results do not depend on it
  *    beyond fp32 rounding order.  The workspace holds the per-split partial
- *    results; its size comes from the matching *_workspace_bytes() call with
- *    the same shape arguments, and may be 0 (then workspace may be NULL).
+ *    results (and, for MLA, the work plan described at kvattn_mla_decode);
+ *    its size comes from the matching *_workspace_bytes() call with the same
+ *    shape arguments, and may be 0 for GQA (then workspace may be NULL).
  *    Its contents need no initialisation.  One workspace serves one call at
  *    a time: calls that share it must be ordered (for example, on one
  *    stream).
@@ -199,6 +200,15 @@ size_t kvattn_gqa_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *               for DeepSeek-V2's head width plus RoPE width).
  *  Supported: dtype bf16, d_latent == 512, d_rope == 64, num_heads a
  *  multiple of 16 up to 128.
+ *
+ *  Work plan.  The call first enqueues a small kernel that reads seq_lens on
+ *  the device and cuts every sequence into pieces of equal length (multiples
+ *  of 32 tokens): with split_tokens = 0, the shortest piece length (at least
+ *  256 tokens) that gives at most max(256, batch) pieces in all, so ragged
+ *  batches keep every compute unit busy; otherwise at most split_tokens
+ *  tokens per piece.  Each piece is one workgroup of the decode kernel;
+ *  sequences with more than one piece are combined by a log-sum-exp merge.
+ *  The plan lives in the workspace, which is therefore never empty.
  */
 kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t* block_table,
                                 const int32_t* seq_lens, void* out, float* lse, int32_t batch,
@@ -217,7 +227,9 @@ size_t kvattn_mla_workspace_bytes(int32_t batch, int32_t num_heads, int32_t d_la
  * contiguous cache, as for the workspace queries).  split_tokens = 0 asks for the library's choice:
  * for a contiguous GQA cache the fewest splits that still give every compute unit two resident
  * workgroups; for a paged one (ragged lengths assumed) about four workgroups per compute unit of
- * at most 2048 tokens each; for MLA about one 128-head workgroup per compute unit. */
+ * at most 2048 tokens each.  For MLA the piece length is chosen on the device from the actual
+ * lengths (see kvattn_mla_decode); kvattn_mla_split_tokens returns the length chosen when every
+ * sequence holds max_seq_len tokens. */
 int32_t kvattn_gqa_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t max_seq_len, int32_t block_size, int32_t split_tokens);
 int32_t kvattn_mla_split_tokens(int32_t batch, int32_t num_heads, int32_t max_seq_len,
@@ -231,7 +243,8 @@ int32_t kvattn_mla_split_tokens(int32_t batch, int32_t num_heads, int32_t max_se
  * Both are hipEvent_t handles the caller created with timing enabled (both
  * non-NULL, or both NULL to disarm).  The setting is consumed by that next
  * call whether or not it succeeds; the log-sum-exp merge kernel the call may
- * add afterwards is outside the two events.
+ * add afterwards, and the MLA plan kernel before it, are outside the two
+ * events.
  */
 kvattn_status kvattn_time_next_kernel(void* start_event, void* stop_event);
 
