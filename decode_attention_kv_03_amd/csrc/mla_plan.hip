@@ -29,17 +29,21 @@ constexpr int kCached = 8;
 
 __device__ __forceinline__ int64_t align32(int64_t x) { return (x + 31) & ~int64_t(31); }
 
+// ceil(a / b) for 0 <= a, b < 2^31 in 32-bit unsigned arithmetic (a + b - 1
+// stays below 2^32; the 64-bit division is several times slower).
+__device__ __forceinline__ uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
+
 // Length of each piece of a sequence of `len` tokens cut for piece length t:
 // ceil(len / t) pieces of equal length, rounded up to the tile.
-__device__ __forceinline__ int64_t piece_len(int64_t len, int64_t t) {
-  const int64_t n = (len + t - 1) / t;
-  return align32((len + n - 1) / n);
+__device__ __forceinline__ int64_t piece_len(int len, uint32_t t) {
+  const uint32_t n = ceil_div((uint32_t)len, t);
+  return align32(ceil_div((uint32_t)len, n));
 }
 
 // Pieces of a sequence of `len` tokens for piece length t (an empty sequence
 // keeps one empty piece).
-__device__ __forceinline__ int64_t pieces_of(int64_t len, int64_t t) {
-  return len > 0 ? (len + t - 1) / t : 1;
+__device__ __forceinline__ int pieces_of(int len, uint32_t t) {
+  return len > 0 ? (int)ceil_div((uint32_t)len, t) : 1;
 }
 
 __device__ __forceinline__ int wave_sum_int(int v) {
@@ -61,6 +65,7 @@ __device__ __forceinline__ int wave_scan_int(int v) {
 
 __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
   const int lane = threadIdx.x;
+  const int rounds = (p.batch + 63) / 64;  // wave-uniform
   int cl[kCached];
 #pragma unroll
   for (int i = 0; i < kCached; ++i) {
@@ -68,27 +73,29 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
     cl[i] = b < p.batch ? clamp_len(p.seq_lens[b], p.len_cap) : -1;  // -1: no sequence
   }
   // Number of pieces for piece length t, saturated at cap + 1 (enough to compare with cap).
-  auto pieces_for = [&](int64_t t, int64_t cap) {
-    int64_t n = 0;
+  auto pieces_for = [&](uint32_t t, int cap) {
+    int n = 0;
 #pragma unroll
     for (int i = 0; i < kCached; ++i)
-      if (cl[i] >= 0) n += pieces_of(cl[i], t);
-    for (int b = lane + 64 * kCached; b < p.batch && n <= cap; b += 64) n += pieces_of(clamp_len(p.seq_lens[b], p.len_cap), t);
-    return wave_sum_int((int)(n < cap + 1 ? n : cap + 1));
+      if (i < rounds && cl[i] >= 0) n = min(n + pieces_of(cl[i], t), cap + 1);
+    for (int b = lane + 64 * kCached; b < p.batch && n <= cap; b += 64)
+      n = min(n + pieces_of(clamp_len(p.seq_lens[b], p.len_cap), t), cap + 1);
+    return wave_sum_int(n);
   };
-  int64_t t = p.fixed_chunk;
-  if (t <= 0) {
+  uint32_t t = p.fixed_chunk > 0 ? (uint32_t)p.fixed_chunk : 0u;  // piece length, up to 2^31
+  if (t == 0) {
     // Shortest multiple of 32 in [min_chunk, len_cap rounded up] with at most
     // cap pieces (the count only falls as t grows, and the upper end gives
     // one piece per sequence).
-    const int64_t cap = p.work_items > p.batch ? p.work_items : p.batch;
-    int64_t lo = p.min_chunk / 32, hi = align32(p.len_cap > p.min_chunk ? p.len_cap : p.min_chunk) / 32;
+    const int cap = p.work_items > p.batch ? p.work_items : p.batch;
+    uint32_t lo = (uint32_t)p.min_chunk / 32;
+    uint32_t hi = (uint32_t)(align32(p.len_cap > p.min_chunk ? p.len_cap : p.min_chunk) / 32);
     while (lo < hi) {
-      const int64_t mid = (lo + hi) / 2;
-      if (pieces_for(32 * mid, cap) <= cap) hi = mid;
+      const uint32_t mid = lo + (hi - lo) / 2;
+      if (pieces_for(32u * mid, cap) <= cap) hi = mid;
       else lo = mid + 1;
     }
-    t = 32 * lo;
+    t = 32u * lo;
   }
 
   // Sequences in rounds of 64; the first piece of each is an exclusive
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
     for (int k = 0; k < kCached; ++k)
       if (k == i) len = cl[k];
     if (i >= kCached && b < p.batch) len = clamp_len(p.seq_lens[b], p.len_cap);
-    const int count = b < p.batch ? (int)pieces_of(len, t) : 0;
+    const int count = b < p.batch ? pieces_of(len, t) : 0;
     const int incl = wave_scan_int(count);
     const int first = carry + incl - count;
     if (b < p.batch) {
@@ -117,7 +124,7 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
   }
   if (lane == 0) {
     p.plan_count[0] = carry;
-    p.plan_count[1] = (int)t;
+    p.plan_count[1] = (int)(t < 0x7fffffffu ? t : 0x7fffffffu);
   }
 }
 
