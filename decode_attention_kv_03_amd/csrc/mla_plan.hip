@@ -46,6 +46,16 @@ __device__ __forceinline__ int pieces_of(int len, uint32_t t) {
   return len > 0 ? (int)ceil_div((uint32_t)len, t) : 1;
 }
 
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const int lo = __shfl_xor((int)(v & 0xffffffff), m, 64);
+    const int hi = __shfl_xor((int)(v >> 32), m, 64);
+    v += ((int64_t)hi << 32) | (uint32_t)lo;
+  }
+  return v;
+}
+
 __device__ __forceinline__ int wave_sum_int(int v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
@@ -90,6 +100,23 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
     const int cap = p.work_items > p.batch ? p.work_items : p.batch;
     uint32_t lo = (uint32_t)p.min_chunk / 32;
     uint32_t hi = (uint32_t)(align32(p.len_cap > p.min_chunk ? p.len_cap : p.min_chunk) / 32);
+    // Closed-form bounds narrow the search: sum ceil(len/t) >= total/t, and
+    // <= total/t + (sequences), so t >= total/cap always and t = total/(cap -
+    // sequences) is enough when cap exceeds the number of sequences.
+    {
+      int64_t tot = 0;
+#pragma unroll
+      for (int i = 0; i < kCached; ++i)
+        if (i < rounds && cl[i] > 0) tot += cl[i];
+      for (int b = lane + 64 * kCached; b < p.batch; b += 64) tot += clamp_len(p.seq_lens[b], p.len_cap);
+      const int64_t total = wave_sum_i64(tot);
+      const uint32_t lb = (uint32_t)(align32((total + cap - 1) / cap) / 32);
+      if (lb > lo) lo = lb < hi ? lb : hi;
+      if (cap > p.batch) {
+        const uint32_t ub = (uint32_t)(align32((total + (cap - p.batch) - 1) / (cap - p.batch)) / 32);
+        if (ub < hi) hi = ub > lo ? ub : lo;
+      }
+    }
     while (lo < hi) {
       const uint32_t mid = lo + (hi - lo) / 2;
       if (pieces_for(32u * mid, cap) <= cap) hi = mid;
@@ -131,8 +158,7 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
 // Log-sum-exp merge of the pieces of each sequence with more than one.
 // Piece q leaves o_q (normalised over its own tokens) and lse_q (log2 of its
 // normaliser); M = max lse_q, w_q = 2^(lse_q - M), o = sum w_q o_q / sum w_q,
-// lse = M + log2 sum w_q.  One wave per (sequence, head); lane l owns
-// output columns 4l .. 4l+3 and 4(l+64) .. 4(l+64)+3.
+// lse = M + log2 sum w_q.  One wave per (sequence, head).
 __global__ __launch_bounds__(64) void mla_merge_pieces(DecodeArgs a) {
   const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int2 sp = a.seq_pieces[b];
@@ -150,19 +176,33 @@ __global__ __launch_bounds__(64) void mla_merge_pieces(DecodeArgs a) {
   const bool empty = !(L > 0.f);
   const float inv = empty ? 0.f : 1.f / L;
 
-  for (int d4 = lane; d4 < kMlaLatent / 4; d4 += 64) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (!empty) {
-      for (int s = 0; s < sp.y; ++s) {
+  // Lane l owns columns 4l .. 4l+3 and 256 + 4l .. +3; pieces are taken four
+  // at a time so eight 16-byte loads per lane are in flight.
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  if (!empty) {
+    for (int s0 = 0; s0 < sp.y; s0 += 4) {
+      f32x4 x0[4], x1[4];
+      float w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = min(s0 + u, sp.y - 1);  // past the last piece: reread it with weight 0
         const int64_t pr = (int64_t)(sp.x + s) * h + head;
-        const float w = fast_exp2(a.part_lse[pr] - M);
-        acc += w * *reinterpret_cast<const f32x4*>(a.part_o + pr * kMlaLatent + 4 * d4);
+        w[u] = s0 + u < sp.y ? fast_exp2(a.part_lse[pr] - M) : 0.f;
+        x0[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kMlaLatent + 4 * lane);
+        x1[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kMlaLatent + 256 + 4 * lane);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc0 += w[u] * x0[u];
+        acc1 += w[u] * x1[u];
       }
     }
-    acc *= inv;
-    uint16_t* o = static_cast<uint16_t*>(a.out) + row * kMlaLatent + 4 * d4;
-    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
   }
+  acc0 *= inv;
+  acc1 *= inv;
+  uint16_t* o = static_cast<uint16_t*>(a.out) + row * kMlaLatent + 4 * lane;
+  *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]));
+  *reinterpret_cast<uint2*>(o + 256) = make_uint2(pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3]));
   if (lane == 0 && a.lse != nullptr) a.lse[row] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
 }
 
