@@ -59,9 +59,9 @@ constexpr int kTileBytes = kT * kRowBytes;     // 36864
 constexpr int kNBuf = 3;                       // LDS ring stages
 constexpr int kWaves = 8;
 constexpr int kTileInsts = kT * kChunks / 64;  // 36 wave-wide copies per tile
-constexpr int kDmaPer = kTileInsts / kWaves;   // 4 ...
-constexpr int kDmaExtra = kTileInsts % kWaves; // ... plus one for the first 4 waves
-static_assert(kDmaPer == 4 && kDmaExtra == 4, "wait counts in the main loop assume 5 / 4 copies per wave");
+constexpr int kCopyWaves = kWaves / 2;        // the lagging group (waves 4-7) issues the copies
+constexpr int kDmaPer = kTileInsts / kCopyWaves;  // 9 per copying wave
+static_assert(kDmaPer * kCopyWaves == kTileInsts && kDmaPer == 9, "wait counts in the main loop assume 9 copies per wave");
 constexpr int kSteps = kMlaRow / 16 / 2;       // 18 score reduction steps per wave
 constexpr int kColBlocks = kMlaLatent / 32 / 2;  // 8 output column blocks per wave
 constexpr int kSxFloats = kWaves * 16 * 64;    // partial-score exchange: 16 floats per lane
@@ -143,13 +143,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   float m_ref = -INFINITY, l_run = 0.f;
 
   const uint16_t* cbase = static_cast<const uint16_t*>(a.k);
-  // Copies of one tile: 36 wave instructions spread over the waves (the
-  // first kDmaExtra waves take one more).  Instruction `inst` fills LDS
+  // Copies of one tile: 36 wave instructions, 9 from each wave of the
+  // lagging group (waves 4-7; see the tile loop).  Instruction `inst` fills LDS
   // block inst: rows 16*(inst/18) + (lane/4) of the tile, slab inst%18, and
   // lane l lands at physical chunk l%4 of its row's slab, which holds
   // logical chunk 4*slab + ((l%4) ^ (l/16)).
-  const int inst0 = wave * kDmaPer + min(wave, kDmaExtra);
-  const int ninst = kDmaPer + (wave < kDmaExtra ? 1 : 0);
+  const int inst0 = (wave - kCopyWaves) * kDmaPer;  // meaningful for the copying waves only
   const int drow = lane >> 2, dchunk = (lane & 3) ^ (lane >> 4);
   // Byte offset of the lane's source inside a 16-row run of cache rows (slab 0).
   const uint32_t doff = (uint32_t)((drow * kRowElems + dchunk * 8) * 2);
@@ -187,8 +186,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
                       : cbase + ((int64_t)e1 * a.block_size + slot_of(a, t0 + 16)) * kRowElems;
       }
 #pragma unroll
-      for (int u = 0; u < kDmaPer + 1; ++u) {
-        if (u < ninst) {
+      for (int u = 0; u < kDmaPer; ++u) {
+        {
           const int inst = inst0 + u;
           const int slab = inst % 18;
           dma16s(doff, base[inst / 18] + slab * 32, dst + inst * 1024);
@@ -201,8 +200,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
     // and the loop keeps its temporaries out of the registers the main loop
     // needs.
 #pragma unroll 1
-    for (int u = 0; u < kDmaPer + 1; ++u) {
-      if (u < ninst) {
+    for (int u = 0; u < kDmaPer; ++u) {
+      {
         const int inst = inst0 + u;
         const int t = min(t0 + 16 * (inst / 18) + drow, t_end - 1);
         const int chunk = 4 * (inst % 18) + dchunk;
@@ -240,34 +239,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 
   const int ntok = t_end - t_begin;
   const int n_tiles = ntok > 0 ? (ntok + kT - 1) / kT : 0;
-  if (n_tiles > 0) issue_tile(t_begin, 0);
+  const bool lead = wave < kWaves - kCopyWaves;  // waves 0-3: the leading group (see the tile loop)
+  if (!lead && n_tiles > 0) issue_tile(t_begin, 0);
   // The queries and the first tile were fetched together (one HBM latency at
   // start-up, not two).  Let both land here: the compiler cannot see the
   // copies in the vector-memory counter, and a wait it placed on the query
   // loads inside the loop would drain the copies in flight every tile.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  if (n_tiles > 1) issue_tile(t_begin + kT, 1);
+  if (!lead && n_tiles > 1) issue_tile(t_begin + kT, 1);
 
-  // One tile: wait for its copies, issue the copies of tile it+2, scores,
-  // partial-score swap, softmax, value product.  kLast marks the last tile
-  // of the piece, the only one that can be ragged; the others are compiled
-  // without any masking.
-  auto tile_step = [&](int it, auto last_tag) __attribute__((always_inline)) {
-    constexpr bool kLast = decltype(last_tag)::value;
-    // Wait for this tile's copies (the next tile's may stay in flight), then
-    // sync; afterwards tile it+2 may go into the stage tile it-1 used.
-    if constexpr (!kLast) {
-      if (wave < kDmaExtra) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (it + 2 < n_tiles) issue_tile(t_begin + (it + 2) * kT, (it + 2) % kNBuf);
-    } else {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    const int t0 = t_begin + it * kT;
+  // Partial scores of tile `it` over this wave's half of the dims, published
+  // in LDS for the other wave of the pair: each lane stores its 16 scores as
+  // four 16-byte words, consecutive across lanes.
+  auto scores = [&](int it) __attribute__((always_inline)) {
     const unsigned char* tile = tiles[it % kNBuf];
-    const auto* tile_lds = (const __attribute__((address_space(3))) unsigned char*)tile;
-
-    // Partial scores over this wave's half of the dims.
     f32x16 s;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = 0.f;
@@ -283,14 +268,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j % kKDepth], qf[j], s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-
-    // Swap partial scores with the other wave of the pair: each lane stores
-    // its 16 scores as four 16-byte words, consecutive across lanes.
     f32x4* mine = reinterpret_cast<f32x4*>(sx) + wave * 4 * 64;
-    const f32x4* other = reinterpret_cast<const f32x4*>(sx) + (wave ^ 1) * 4 * 64;
 #pragma unroll
     for (int q = 0; q < 4; ++q) mine[q * 64 + lane] = f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    return s;
+  };
+
+  // Softmax and value product of tile `it`, from this wave's partial scores
+  // `s` and the partner's published ones.  kLast marks the last tile of the
+  // piece, the only one that can be ragged; the others are compiled without
+  // any masking.
+  auto softmax_values = [&](int it, const f32x16& s, auto last_tag) __attribute__((always_inline)) {
+    constexpr bool kLast = decltype(last_tag)::value;
+    const int t0 = t_begin + it * kT;
+    const auto* tile_lds = (const __attribute__((address_space(3))) unsigned char*)tiles[it % kNBuf];
+    const f32x4* other = reinterpret_cast<const f32x4*>(sx) + (wave ^ 1) * 4 * 64;
     float sv[16];  // raw scores q.k
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -302,10 +294,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 
     // Online softmax on c * score (c = scale * log2 e, log2 units); P^T is
     // packed straight into the B-operand layout.  The tile maximum of c * s
-    // is c times the raw maximum (the minimum, for a negative scale).  Only
-    // the last tile of a piece can hold tokens past its end; its masked
-    // scores are set to the neutral element of that extremum and their
-    // probabilities to zero.
+    // is c times the raw maximum (the minimum, for a negative scale).  Masked
+    // scores of a ragged last tile are set to the neutral element of that
+    // extremum and their probabilities to zero.
     const float c = a.scale_log2;
     const float neutral = c >= 0.f ? -INFINITY : INFINITY;
     if constexpr (kLast) {
@@ -378,8 +369,51 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int it = 0; it + 1 < n_tiles; ++it) tile_step(it, TagFalse{});
-  if (n_tiles > 0) tile_step(n_tiles - 1, TagTrue{});
+
+  // Two wave groups, one interval apart.  Waves 0-3 (pairs 0 and 1) and
+  // waves 4-7 (pairs 2 and 3) share the SIMDs (wave w runs on SIMD w % 4).
+  // A tile takes two intervals between workgroup barriers: the leading group
+  // computes its partial scores in the first and its softmax and value
+  // product in the second; the lagging group does its scores in the second
+  // interval and the rest in the next tile's first.  On every SIMD one
+  // wave's score products then run beside the other wave's softmax and value
+  // products instead of all waves doing the same phase at once.  The
+  // interval boundaries double as the pairs' partial-score swaps.  The
+  // lagging group issues all copies: those of tile it+2 right after the
+  // second barrier of tile it, when every wave is done with tile it-1, whose
+  // stage they overwrite, and it waits for tile it's copies before the first
+  // barrier of tile it.  Both groups pass the same barriers in the same
+  // order: two per tile and one after the last.
+  if (lead) {
+    auto lead_tile = [&](int it, auto last_tag) __attribute__((always_inline)) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // tile it has landed
+      const f32x16 s = scores(it);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // partial scores published
+      softmax_values(it, s, last_tag);
+    };
+    for (int it = 0; it + 1 < n_tiles; ++it) lead_tile(it, TagFalse{});
+    if (n_tiles > 0) {
+      lead_tile(n_tiles - 1, TagTrue{});
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  } else {
+    f32x16 s;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = 0.f;
+    for (int it = 0; it < n_tiles; ++it) {
+      // Tile it's copies have landed (tile it+1's may stay in flight).
+      if (it + 1 < n_tiles) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (it > 0) softmax_values(it - 1, s, TagFalse{});
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (it + 2 < n_tiles) issue_tile(t_begin + (it + 2) * kT, (it + 2) % kNBuf);
+      s = scores(it);
+    }
+    if (n_tiles > 0) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // partial scores of the last tile published
+      softmax_values(n_tiles - 1, s, TagTrue{});
+    }
+  }
 
   // Lane l holds O^T[col = 32*cb + 8*(v/4) + 4*(l/32) + v%4][head 32*pair + l%32].
   const int head = 32 * pair + c32;
