@@ -417,13 +417,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 
   // Lane l holds O^T[col = 32*cb + 8*(v/4) + 4*(l/32) + v%4][head 32*pair + l%32].
   const int head = 32 * pair + c32;
-  if (head >= h) return;
   const float l = sum_over_halves(l_run);
   const int64_t row = (int64_t)b * h + head;
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.f / l;
   const float lse2 = empty ? -INFINITY : m_ref + __log2f(l);
   if (final_out) {
+    if (head >= h) return;
     uint16_t* o = static_cast<uint16_t*>(a.out) + row * kMlaLatent + 4 * g;
 #pragma unroll
     for (int i = 0; i < kColBlocks; ++i)
@@ -434,17 +434,40 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
         *reinterpret_cast<uint2*>(o + 32 * (2 * i + half) + 8 * q) = make_uint2(lo, hi);
       }
     if (a.lse != nullptr && g == 0 && half == 0) a.lse[row] = lse2 * kLn2;
-  } else {
-    const int64_t prow = (int64_t)piece * h + head;
-    float* po = a.part_o + prow * kMlaLatent + 4 * g;
-#pragma unroll
-    for (int i = 0; i < kColBlocks; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(po + 32 * (2 * i + half) + 8 * q) =
-            f32x4{acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]} * inv;
-    if (g == 0 && half == 0) a.part_lse[prow] = lse2;
+    return;
   }
+  // Partial: staged through LDS so that every store instruction writes whole
+  // 128-byte lines (the accumulator layout would write 32-byte pieces of 32
+  // head rows).  Each wave has its own region of the (now idle) tile ring:
+  // 32 head rows of 64 columns, rows padded to 68 floats so that both the
+  // row-per-lane writes and the line-per-8-lanes reads are conflict-free.
+  // Four rounds of two column blocks each.
+  constexpr int kStgPitch = 68;
+  __syncthreads();  // every wave is done with the tile ring
+  float* stg = reinterpret_cast<float*>(&tiles[0][0]) + wave * (32 * kStgPitch);
+  const int64_t prow0 = (int64_t)piece * h + 32 * pair;  // partial row of this wave's first head
+#pragma unroll
+  for (int k = 0; k < kColBlocks / 2; ++k) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& x = acc[2 * k + jj];
+        *reinterpret_cast<f32x4*>(stg + c32 * kStgPitch + 32 * jj + 8 * q + 4 * g) =
+            f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]} * inv;
+      }
+    // Line m*8 + lane/8 of the round: head row (line / 2), column block 2k + (line % 2) of this wave.
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int line = 8 * m + (lane >> 3);
+      const int hh = line >> 1, jb = line & 1;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + hh * kStgPitch + 32 * jb + 4 * (lane & 7));
+      if (32 * pair + hh < h)
+        *reinterpret_cast<f32x4*>(a.part_o + (prow0 + hh) * kMlaLatent + 32 * (2 * (2 * k + jb) + half) +
+                                  4 * (lane & 7)) = v;
+    }
+  }
+  if (head < h && g == 0 && half == 0) a.part_lse[prow0 + c32] = lse2;
 }
 
 }  // namespace
