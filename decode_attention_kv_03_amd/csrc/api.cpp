@@ -94,7 +94,7 @@ int64_t mla_max_pieces(int32_t batch, int32_t max_seq_len, int32_t requested) {
   return n > (int64_t)INT32_MAX / 8 ? -1 : n;
 }
 
-// Workspace regions of an MLA call: partial outputs, partial log-sum-exps, the plan's pieces,
+// Workspace regions of an MLA call: partial outputs (bf16), partial log-sum-exps (fp32), the plan's pieces,
 // per-sequence piece ranges and the plan's counts, each 256-byte aligned.
 struct MlaWorkspace {
   size_t part_o, part_lse, pieces, seq_pieces, plan_count, total;
@@ -102,7 +102,7 @@ struct MlaWorkspace {
 MlaWorkspace mla_workspace(int64_t batch, int64_t heads, int64_t max_pieces, int64_t d_c) {
   MlaWorkspace w{};
   w.part_o = 0;
-  w.part_lse = w.part_o + (size_t)round_up(max_pieces * heads * d_c * (int64_t)sizeof(float), 256);
+  w.part_lse = w.part_o + (size_t)round_up(max_pieces * heads * d_c * 2, 256);  // bf16 partial outputs
   w.pieces = w.part_lse + (size_t)round_up(max_pieces * heads * (int64_t)sizeof(float), 256);
   w.seq_pieces = w.pieces + (size_t)round_up(max_pieces * 16, 256);
   w.plan_count = w.seq_pieces + (size_t)round_up(batch * 8, 256);

@@ -32,7 +32,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   void* out;
   float* lse;               // may be null
-  float* part_o;            // [B, h, n_split, d_v] fp32 partial outputs (normalised); null if n_split == 1
+  float* part_o;            // GQA: [B, h, n_split, d_v] fp32 partial outputs (normalised), null if n_split == 1;
+                            // MLA: bf16, per piece (below)
   float* part_lse;          // [B, h, n_split] log2-domain log-sum-exp of each split
   int32_t batch;
   int32_t num_q_heads;      // h
@@ -51,7 +52,7 @@ struct DecodeArgs {
   // MLA work plan, written on the device by the plan kernel:
   //   pieces[q] = (sequence, first token, end token, 1 if it is the sequence's only piece)
   //   seq_pieces[b] = (first piece, number of pieces); plan_count = {pieces, piece length}
-  // Partials of piece q, head i: part_o[(q * h + i) * d_v], part_lse[q * h + i].
+  // Partials of piece q, head i: part_o[(q * h + i) * d_v] (bf16 for MLA), part_lse[q * h + i].
   const int4* pieces;
   const int2* seq_pieces;
   const int32_t* plan_count;

@@ -16,7 +16,8 @@
 // A workgroup (8 waves, two per SIMD) owns one piece of a sequence (a run
 // of its tokens, from the device-side plan in mla_plan.hip) and all heads.  Waves pair up per 32-head block: each wave of a pair holds the
 // query for half of the 576 dims (18 reduction steps of 16) and the output
-// accumulators for half of the 512 latent columns (8 blocks of 32), which
+// accumulators for one half of the 512 latent columns (8 blocks of 32: the
+// lower 256 columns for the first wave, the upper for the second), which
 // keeps both under the 256 registers a wave has at two waves per SIMD.  The
 // pair swaps partial scores through LDS once per tile.
 //
@@ -230,9 +231,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   // 4*(G/2) + n/4 (+8 for the second run, +16*kk) and the four columns
   // 32*cb + 16*(G%2) + 4*(n%4) .. +3 (chunk 4*cb + 2*(G%2) + (n%4)/2, byte
   // 8*(n%2)), and receives column 32*cb + 16*(G%2) + n.  Column block
-  // cb = 2*i + half adds an immediate 2048 * i, step kk one of 16 rows.
+  // cb = 8*half + i adds an immediate 1024 * i, step kk one of 16 rows.
   const int vn = lane & 15, vgrp = lane >> 4;
-  const int vchunk = 4 * half + 2 * (vgrp & 1) + ((vn & 3) >> 1);
+  const int vchunk = 32 * half + 2 * (vgrp & 1) + ((vn & 3) >> 1);
   const int vrow0 = 4 * (vgrp >> 1) + (vn >> 2);
   const int voff0 = lds_chunk(vrow0, vchunk) + 8 * (vn & 1);
   const int voff1 = lds_chunk(vrow0 + 8, vchunk) + 8 * (vn & 1);
@@ -347,11 +348,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
     }
 
     // Values: O^T[32 cols x 32 heads] += V^T[32 cols x 16 tokens] * P^T per
-    // step kk, for this wave's column blocks cb = 2*i + half (latent columns
+    // step kk, for this wave's column blocks cb = 8*half + i (latent columns
     // 32*cb .. 32*cb+31).  Steps run kk-major, so consecutive matrix ops
     // accumulate into different blocks.
     auto read_v = [&](int i, int kk) __attribute__((always_inline)) {
-      const int imm = 2048 * i + (kTileBytes / 2) * kk;
+      const int imm = 1024 * i + (kTileBytes / 2) * kk;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_lds + voff0 + imm));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_lds + voff1 + imm));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -431,40 +432,44 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
       for (int q = 0; q < 4; ++q) {
         const uint32_t lo = pack_bf16x2(acc[i][4 * q] * inv, acc[i][4 * q + 1] * inv);
         const uint32_t hi = pack_bf16x2(acc[i][4 * q + 2] * inv, acc[i][4 * q + 3] * inv);
-        *reinterpret_cast<uint2*>(o + 32 * (2 * i + half) + 8 * q) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(o + 32 * (8 * half + i) + 8 * q) = make_uint2(lo, hi);
       }
     if (a.lse != nullptr && g == 0 && half == 0) a.lse[row] = lse2 * kLn2;
     return;
   }
-  // Partial: staged through LDS so that every store instruction writes whole
-  // 128-byte lines (the accumulator layout would write 32-byte pieces of 32
-  // head rows).  Each wave has its own region of the (now idle) tile ring:
-  // 32 head rows of 64 columns, rows padded to 68 floats so that both the
-  // row-per-lane writes and the line-per-8-lanes reads are conflict-free.
-  // Four rounds of two column blocks each.
-  constexpr int kStgPitch = 68;
+  // Partial output, normalised and rounded to bf16 (the merge weighs the
+  // pieces in fp32 from their fp32 log-sum-exps): staged through LDS so that
+  // every store instruction writes whole 128-byte lines (the accumulator
+  // layout would write 8-byte pieces of 32 head rows).  Each wave has its own
+  // region of the (now idle) tile ring: 32 head rows of 128 columns (256
+  // bytes), rows padded to 272 bytes (16-byte aligned, and the line-per-8-lanes
+  // reads conflict-free).  Two rounds of four column blocks each, over the
+  // wave's columns 256*half .. 256*half+255.
+  constexpr int kStgPitch = 272;  // bytes
   __syncthreads();  // every wave is done with the tile ring
-  float* stg = reinterpret_cast<float*>(&tiles[0][0]) + wave * (32 * kStgPitch);
+  unsigned char* stg = &tiles[0][0] + wave * (32 * kStgPitch);
+  uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o);
   const int64_t prow0 = (int64_t)piece * h + 32 * pair;  // partial row of this wave's first head
 #pragma unroll
-  for (int k = 0; k < kColBlocks / 2; ++k) {
+  for (int k = 0; k < kColBlocks / 4; ++k) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x16& x = acc[2 * k + jj];
-        *reinterpret_cast<f32x4*>(stg + c32 * kStgPitch + 32 * jj + 8 * q + 4 * g) =
-            f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]} * inv;
+        const f32x16& x = acc[4 * k + jj];
+        *reinterpret_cast<uint2*>(stg + c32 * kStgPitch + 2 * (32 * jj + 8 * q + 4 * g)) =
+            make_uint2(pack_bf16x2(x[4 * q] * inv, x[4 * q + 1] * inv),
+                       pack_bf16x2(x[4 * q + 2] * inv, x[4 * q + 3] * inv));
       }
-    // Line m*8 + lane/8 of the round: head row (line / 2), column block 2k + (line % 2) of this wave.
+    // Line 8*m + lane/8 of the round: head row line/2, columns 64*(line%2) .. +63 of the round's 128.
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int line = 8 * m + (lane >> 3);
       const int hh = line >> 1, jb = line & 1;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + hh * kStgPitch + 32 * jb + 4 * (lane & 7));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + hh * kStgPitch + 128 * jb + 16 * (lane & 7));
       if (32 * pair + hh < h)
-        *reinterpret_cast<f32x4*>(a.part_o + (prow0 + hh) * kMlaLatent + 32 * (2 * (2 * k + jb) + half) +
-                                  4 * (lane & 7)) = v;
+        *reinterpret_cast<u32x4*>(po + (prow0 + hh) * kMlaLatent + 256 * half + 128 * k + 64 * jb +
+                                  8 * (lane & 7)) = v;
     }
   }
   if (head < h && g == 0 && half == 0) a.part_lse[prow0 + c32] = lse2;

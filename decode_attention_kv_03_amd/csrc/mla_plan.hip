@@ -23,6 +23,12 @@
 namespace kvattn {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The two bf16 values packed in a 32-bit word, widened to fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 // The plan runs as one wave: lane l handles sequences l, l+64, ...; the
 // lengths of the first kCached rounds stay in registers across the search.
 constexpr int kCached = 8;
@@ -156,8 +162,8 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
 }
 
 // Log-sum-exp merge of the pieces of each sequence with more than one.
-// Piece q leaves o_q (normalised over its own tokens) and lse_q (log2 of its
-// normaliser); M = max lse_q, w_q = 2^(lse_q - M), o = sum w_q o_q / sum w_q,
+// Piece q leaves o_q (normalised over its own tokens, rounded to bf16) and
+// lse_q (fp32, log2 of its normaliser); M = max lse_q, w_q = 2^(lse_q - M), o = sum w_q o_q / sum w_q,
 // lse = M + log2 sum w_q.  One wave per (sequence, head).
 __global__ __launch_bounds__(64) void mla_merge_pieces(DecodeArgs a) {
   const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
@@ -176,33 +182,34 @@ __global__ __launch_bounds__(64) void mla_merge_pieces(DecodeArgs a) {
   const bool empty = !(L > 0.f);
   const float inv = empty ? 0.f : 1.f / L;
 
-  // Lane l owns columns 4l .. 4l+3 and 256 + 4l .. +3; pieces are taken four
-  // at a time so eight 16-byte loads per lane are in flight.
+  // Partial outputs are bf16 [piece, head, 512].  Lane l owns columns 8l ..
+  // 8l+7 (one 16-byte load per piece); pieces are taken eight at a time so
+  // eight loads per lane are in flight.
+  const uint16_t* po = reinterpret_cast<const uint16_t*>(a.part_o);
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
   if (!empty) {
-    for (int s0 = 0; s0 < sp.y; s0 += 4) {
-      f32x4 x0[4], x1[4];
-      float w[4];
+    for (int s0 = 0; s0 < sp.y; s0 += 8) {
+      u32x4 x[8];
+      float w[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int s = min(s0 + u, sp.y - 1);  // past the last piece: reread it with weight 0
         const int64_t pr = (int64_t)(sp.x + s) * h + head;
         w[u] = s0 + u < sp.y ? fast_exp2(a.part_lse[pr] - M) : 0.f;
-        x0[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kMlaLatent + 4 * lane);
-        x1[u] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kMlaLatent + 256 + 4 * lane);
+        x[u] = *reinterpret_cast<const u32x4*>(po + pr * kMlaLatent + 8 * lane);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc0 += w[u] * x0[u];
-        acc1 += w[u] * x1[u];
+      for (int u = 0; u < 8; ++u) {
+        acc0 += w[u] * f32x4{bf16_lo(x[u][0]), bf16_hi(x[u][0]), bf16_lo(x[u][1]), bf16_hi(x[u][1])};
+        acc1 += w[u] * f32x4{bf16_lo(x[u][2]), bf16_hi(x[u][2]), bf16_lo(x[u][3]), bf16_hi(x[u][3])};
       }
     }
   }
   acc0 *= inv;
   acc1 *= inv;
-  uint16_t* o = static_cast<uint16_t*>(a.out) + row * kMlaLatent + 4 * lane;
-  *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]));
-  *reinterpret_cast<uint2*>(o + 256) = make_uint2(pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3]));
+  uint16_t* o = static_cast<uint16_t*>(a.out) + row * kMlaLatent + 8 * lane;
+  *reinterpret_cast<u32x4*>(o) = u32x4{pack_bf16x2(acc0[0], acc0[1]), pack_bf16x2(acc0[2], acc0[3]),
+                                       pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
   if (lane == 0 && a.lse != nullptr) a.lse[row] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
 }
 

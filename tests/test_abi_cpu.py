@@ -135,12 +135,13 @@ def _mla_workspace(batch, heads, pieces, d_c=512):
     def up(x):
         return (x + 255) // 256 * 256
 
-    return up(pieces * heads * d_c * 4) + up(pieces * heads * 4) + up(pieces * 16) + up(batch * 8) + 256
+    # bf16 partial outputs, fp32 partial log-sum-exps, the plan's pieces, per-sequence ranges, counts
+    return up(pieces * heads * d_c * 2) + up(pieces * heads * 4) + up(pieces * 16) + up(batch * 8) + 256
 
 
 def test_mla_workspace_bytes():
     # pieces of the device-side plan: at most max(256, batch) (one per compute unit, or per sequence),
-    # each with fp32 partial outputs (512 wide) and log-sum-exps for every head, plus the plan itself
+    # each with bf16 partial outputs (512 wide) and fp32 log-sum-exps for every head, plus the plan itself
     assert lib.kvattn_mla_workspace_bytes(32, 128, 512, 64, 8192, 0, 0, K.KVATTN_BF16) == _mla_workspace(32, 128, 256)
     assert lib.kvattn_mla_workspace_bytes(300, 128, 512, 64, 64, 0, 0, K.KVATTN_BF16) == _mla_workspace(300, 128, 300)
     # a requested piece length bounds the pieces by ceil(max_seq_len / split) per sequence
