@@ -162,37 +162,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   // multiples of 32 tokens).  The ragged last tile of a piece takes the
   // general path, which clamps every row into the piece.
   const bool halves_contiguous = a.block_size == 0 || (a.block_size & 15) == 0;
+  // First cache row of the 16-row run starting at token t (a multiple of 16;
+  // fast path only).  A paged lookup is a scalar table load (counted by
+  // lgkmcnt, so the copies in flight are left alone).
+  auto half_base = [&](int t) __attribute__((always_inline)) -> const uint16_t* {
+    if (a.block_size == 0) return seq_base + (int64_t)t * kRowElems;
+    const int32_t* ep = tbl + block_of(a, t);
+    int e;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(e) : "s"(ep) : "memory");
+    // An out-of-range table entry reads the pool's first rows instead.
+    return (e < 0 || (int64_t)e >= a.cache_len) ? cbase
+                                                : cbase + ((int64_t)e * a.block_size + slot_of(a, t)) * kRowElems;
+  };
   auto issue_tile = [&](int t0, int buf) __attribute__((always_inline)) {
     const uint32_t dst = (uint32_t)(uintptr_t)&tiles[buf][0];
     if (halves_contiguous && t0 + kT <= t_end) {
-      const uint16_t* base[2];
-      if (a.block_size == 0) {
-        base[0] = seq_base + (int64_t)t0 * kRowElems;
-        base[1] = base[0] + 16 * kRowElems;
-      } else {
-        // Scalar table loads (counted by lgkmcnt) leave the copies in flight alone.
-        const int32_t* ep0 = tbl + block_of(a, t0);
-        const int32_t* ep1 = tbl + block_of(a, t0 + 16);
-        int e0, e1;
-        asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&s"(e0), "=&s"(e1)
-                     : "s"(ep0), "s"(ep1)
-                     : "memory");
-        // An out-of-range table entry reads the pool's first rows instead.
-        base[0] = (e0 < 0 || (int64_t)e0 >= a.cache_len)
-                      ? cbase
-                      : cbase + ((int64_t)e0 * a.block_size + slot_of(a, t0)) * kRowElems;
-        base[1] = (e1 < 0 || (int64_t)e1 >= a.cache_len)
-                      ? cbase
-                      : cbase + ((int64_t)e1 * a.block_size + slot_of(a, t0 + 16)) * kRowElems;
-      }
+      // This wave's nine instructions lie in one 16-row half of the tile.
+      const uint16_t* hb = half_base(t0 + 16 * (inst0 / 18));
 #pragma unroll
       for (int u = 0; u < kDmaPer; ++u) {
-        {
-          const int inst = inst0 + u;
-          const int slab = inst % 18;
-          dma16s(doff, base[inst / 18] + slab * 32, dst + inst * 1024);
-        }
+        const int inst = inst0 + u;
+        dma16s(doff, hb + (inst % 18) * 32, dst + inst * 1024);
       }
       return;
     }
@@ -251,8 +241,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 
   // Partial scores of tile `it` over this wave's half of the dims, published
   // in LDS for the other wave of the pair: each lane stores its 16 scores as
-  // four 16-byte words, consecutive across lanes.
-  auto scores = [&](int it) __attribute__((always_inline)) {
+  // four 16-byte words, consecutive across lanes.  copy(u) runs after every
+  // second matrix op (u = 0..8), so that a copying wave's nine copy
+  // instructions are spread over its score products: issued in one burst
+  // they hold the wave for about as long as the products take, since the
+  // compute unit accepts copies only at the rate it moves their data.
+  auto scores = [&](int it, auto copy) __attribute__((always_inline)) {
     const unsigned char* tile = tiles[it % kNBuf];
     f32x16 s;
 #pragma unroll
@@ -267,6 +261,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
     for (int j = 0; j < kSteps; ++j) {
       if (j + kKDepth - 1 < kSteps) ka[(j + kKDepth - 1) % kKDepth] = read_k(j + kKDepth - 1);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[j % kKDepth], qf[j], s, 0, 0, 0);
+      if (j % 2 == 1) copy(j / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     f32x4* mine = reinterpret_cast<f32x4*>(sx) + wave * 4 * 64;
@@ -388,7 +383,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   if (lead) {
     auto lead_tile = [&](int it, auto last_tag) __attribute__((always_inline)) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // tile it has landed
-      const f32x16 s = scores(it);
+      const f32x16 s = scores(it, [](int) {});
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // partial scores published
       softmax_values(it, s, last_tag);
     };
@@ -407,8 +402,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
       else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       if (it > 0) softmax_values(it - 1, s, TagFalse{});
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (it + 2 < n_tiles) issue_tile(t_begin + (it + 2) * kT, (it + 2) % kNBuf);
-      s = scores(it);
+      // Copies of tile it+2, into the stage tile it-1 held.
+      const int tn = t_begin + (it + 2) * kT;
+      if (it + 2 < n_tiles && halves_contiguous && tn + kT <= t_end) {
+        const uint16_t* hb = half_base(tn + 16 * (inst0 / 18));
+        const uint32_t dst = (uint32_t)(uintptr_t)&tiles[(it + 2) % kNBuf][0] + inst0 * 1024;
+        const int slab0 = inst0 % 18;
+        s = scores(it, [&](int u) __attribute__((always_inline)) {
+          dma16s(doff, hb + (slab0 + u) * 32, dst + u * 1024);
+        });
+      } else {
+        if (it + 2 < n_tiles) issue_tile(tn, (it + 2) % kNBuf);
+        s = scores(it, [](int) {});
+      }
     }
     if (n_tiles > 0) {
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // partial scores of the last tile published
