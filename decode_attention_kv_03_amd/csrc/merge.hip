@@ -6,8 +6,7 @@
 // scaled scores).  The exact result over all tokens is
 //     M = max_s lse_s,  w_s = 2^(lse_s - M),  o = sum_s w_s o_s / sum_s w_s,
 //     lse = M + log2(sum_s w_s)
-// (softmax over a union of token sets).  One wave per (sequence, head);
-// lane l owns output columns 4l..4l+3 (and 4(l+64).. for d_v = 512).
+// (softmax over a union of token sets).  One wave per (sequence, head).
 #include "device_common.h"
 #include "kvattn_internal.h"
 
@@ -16,7 +15,18 @@ namespace {
 
 template <int DV, bool BF16_OUT>
 __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
+  // Lane l handles float4 columns c = l % kRowLanes (+ kRowLanes * k) of
+  // the splits s = l / kRowLanes + kSplitGroups * u.  Every load of a round
+  // (the splits' log-sum-exps and partial outputs) is issued before any is
+  // used, so a round costs one memory latency; one round covers up to
+  // kSplitGroups * kU splits.
+  constexpr int kVec = DV / 4;                        // float4 columns per row
+  constexpr int kRowLanes = kVec < 64 ? kVec : 64;    // lanes across a row
+  constexpr int kSplitGroups = 64 / kRowLanes;        // splits read side by side
+  constexpr int kCols = kVec / kRowLanes;             // float4 columns per lane
+  constexpr int kU = 8;                               // splits per lane and round
   const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int c = lane % kRowLanes, sg = lane / kRowLanes;
   const int len = clamp_len(a.seq_lens[b], a.len_cap);
   int nv = (len - window_base(len, a.window) + a.split_tokens - 1) / a.split_tokens;
   nv = min(nv, a.n_split);
@@ -24,32 +34,68 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
   const float* pl = a.part_lse + row * a.n_split;
   const float* po = a.part_o + row * a.n_split * DV;
 
-  float M = -INFINITY;
-  for (int s = lane; s < nv; s += 64) M = fmaxf(M, pl[s]);
+  // Loads of one round: splits s0 + sg + kSplitGroups * u (past the last
+  // split: the last one again, weighted 0 below).
+  f32x4 x[kU][kCols];
+  float ls[kU];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int s = min(s0 + sg + kSplitGroups * u, nv - 1);
+      ls[u] = pl[s];
+#pragma unroll
+      for (int k = 0; k < kCols; ++k)
+        x[u][k] = *reinterpret_cast<const f32x4*>(po + (int64_t)s * DV + 4 * (c + kRowLanes * k));
+    }
+  };
+  if (nv > 0) load_round(0);  // in flight while the maximum and the normaliser are found
+
+  // Lane l keeps the log-sum-exp of split l; splits past 64 are reread.
+  const float lv = lane < nv ? pl[lane] : -INFINITY;
+  float M = lv;
+  for (int s = lane + 64; s < nv; s += 64) M = fmaxf(M, pl[s]);
   M = wave_reduce_max(M);
   float L = 0.f;
-  if (M != -INFINITY)
-    for (int s = lane; s < nv; s += 64) L += fast_exp2(pl[s] - M);
+  if (M != -INFINITY) {
+    L = lane < nv ? fast_exp2(lv - M) : 0.f;
+    for (int s = lane + 64; s < nv; s += 64) L += fast_exp2(pl[s] - M);
+  }
   L = wave_reduce_sum(L);
   const bool empty = !(L > 0.f);
   const float inv = empty ? 0.f : 1.f / L;
 
-  for (int d4 = lane; d4 < DV / 4; d4 += 64) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (!empty) {
-      for (int s = 0; s < nv; ++s) {
-        const float w = fast_exp2(pl[s] - M);
-        acc += w * *reinterpret_cast<const f32x4*>(po + (int64_t)s * DV + 4 * d4);
+  f32x4 acc[kCols];
+#pragma unroll
+  for (int k = 0; k < kCols; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (!empty) {
+    for (int s0 = 0; s0 < nv; s0 += kSplitGroups * kU) {
+      if (s0 > 0) load_round(s0);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float w = s0 + sg + kSplitGroups * u < nv ? fast_exp2(ls[u] - M) : 0.f;
+#pragma unroll
+        for (int k = 0; k < kCols; ++k) acc[k] += w * x[u][k];
       }
     }
-    acc *= inv;
-    if constexpr (BF16_OUT) {
-      uint16_t* o = static_cast<uint16_t*>(a.out) + row * DV + 4 * d4;
-      const uint32_t lo = pack_bf16x2(acc[0], acc[1]);
-      const uint32_t hi = pack_bf16x2(acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * DV + 4 * d4) = acc;
+  }
+  // Lanes of the other split groups hold the other splits' sums for the same columns.
+#pragma unroll
+  for (int m = kRowLanes; m < 64; m <<= 1)
+#pragma unroll
+    for (int k = 0; k < kCols; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[k][e] += __shfl_xor(acc[k][e], m, 64);
+  if (sg == 0) {
+#pragma unroll
+    for (int k = 0; k < kCols; ++k) {
+      const f32x4 o4 = acc[k] * inv;
+      const int64_t off = row * DV + 4 * (c + kRowLanes * k);
+      if constexpr (BF16_OUT) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
+            make_uint2(pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3]));
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + off) = o4;
+      }
     }
   }
   if (lane == 0 && a.lse != nullptr) a.lse[row] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
