@@ -261,10 +261,11 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
 
-    # Timed region 1 (the headline): HIP events around each whole call on the stream the kernels run
-    # on, and wall time around the loop.  Timed region 2: the same K steps again with HIP events
-    # around each call's split-K kernel alone (kvattn_time_next_kernel), for the kernel roofline;
-    # it is kept apart because the extra event packets cost a few microseconds per call.
+    # Timed region 1 (the headline): the K calls back to back, wall time between two
+    # synchronisations, nothing else on the stream.  Region 2: the same K calls with HIP events
+    # around each whole call on the stream the kernels run on.  Region 3: HIP events around each
+    # call's split-K kernel alone (kvattn_time_next_kernel), for the kernel roofline.  They are kept
+    # apart because event packets between the calls cost a few microseconds each.
     def events(n):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         for e in evs:
@@ -275,11 +276,14 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(args.steps):
         starts[i].record(stream)
         step(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     for i in range(args.steps):
         time_next_kernel(kstarts[i], kends[i])
         step(i)
