@@ -3,6 +3,7 @@
     python -m decode_attention_kv_03_amd.profiling trace STATS_CSV OUT_MD TITLE COMMAND
     python -m decode_attention_kv_03_amd.profiling traffic WORKLOAD OUT_MD FETCH_DIR WRITE_DIR \
         COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES COMMANDS
+    python -m decode_attention_kv_03_amd.profiling mfma WORKLOAD OUT_MD RUN_DIR TRACE_MD ALGO_FLOPS COMMAND
 
 ``trace`` condenses a ``--kernel-trace --stats`` kernel_stats.csv into a table
 of the library's kernels.  ``traffic`` turns two ``--pmc`` runs of a workload
@@ -10,7 +11,10 @@ of the library's kernels.  ``traffic`` turns two ``--pmc`` runs of a workload
 the split-K kernel, each scaled by what the same counter reads for a plain
 device copy of known size, and records the hash of the kernel sources the
 counters were taken with.  ``bench.py`` reports that traffic only while the
-sources still hash the same.
+sources still hash the same.  ``mfma`` turns one ``--pmc MfmaUtil
+MfmaFlopsBF16 GRBM_GUI_ACTIVE`` run into the split-K kernel's counted
+matrix-core FLOPs, busy fraction and effective clock, with the kernel's mean
+duration taken from its kernel-trace summary.
 """
 
 import csv
@@ -112,6 +116,61 @@ def summarize_traffic(workload, out_md, fetch_dir, write_dir, copy_fetch_dir, co
                 f"write_bytes={write_b:.0f} -->\n")
 
 
+# Matrix-core rate of one MI355X compute unit at bf16: 4 SIMDs x 1024 FLOP per clock.
+BF16_FLOP_PER_CLK_PER_CU = 4096
+CUS = 256
+XCDS = 8
+BF16_PEAK_FLOPS = 2.5e15
+
+
+def _trace_split_us(trace_md):
+    with open(trace_md) as fh:
+        for line in fh:
+            m = re.match(r"\| `(.*?)` \| \d+ \| ([\d.]+) \|", line)
+            if m and _is_split(m.group(1)):
+                return float(m.group(2))
+    raise ValueError(f"no split-K kernel row in {trace_md}")
+
+
+def _mean_dispatch_ns(run_dir, match):
+    """Mean (End - Start) timestamp of the matching dispatches of a counter run."""
+    seen = {}
+    for r in _counter_rows(run_dir):
+        if match(r["Kernel_Name"]):
+            seen[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return sum(seen.values()) / len(seen)
+
+
+def summarize_mfma(workload, out_md, run_dir, trace_md, algo_flops, command):
+    flops, n = _mean_counter(run_dir, "MfmaFlopsBF16", _is_split)
+    util, _ = _mean_counter(run_dir, "MfmaUtil", _is_split)
+    gui, _ = _mean_counter(run_dir, "GRBM_GUI_ACTIVE", _is_split)
+    run_ns = _mean_dispatch_ns(run_dir, _is_split)
+    us = _trace_split_us(trace_md)
+    # GRBM_GUI_ACTIVE counts the clocks the GPU was busy during the dispatch, and the
+    # collection sums it over the XCDs (each has its own GRBM; the MfmaUtil expression
+    # takes their maximum instead), so one XCD's clocks are the sum / 8.
+    clk = gui / XCDS / (run_ns * 1e-9)
+    at_clock = algo_flops / (us * 1e-6) / (CUS * BF16_FLOP_PER_CLK_PER_CU * clk)
+    with open(out_md, "w") as f:
+        f.write(f"# Matrix-core counters of the split-K kernel: {workload}\n\n")
+        f.write("rocprofv3 counter run, from the repository root on one MI355X (the kernel's mean duration is\n"
+                f"the split-K row of `{os.path.relpath(trace_md, os.path.dirname(PROFILES))}`):\n\n")
+        f.write("```\n" + command + "\n```\n\n")
+        f.write("| quantity | value |\n|---|---|\n")
+        f.write(f"| MfmaFlopsBF16 per dispatch (GFLOP, mean of {n}) | {flops / 1e9:.3f} |\n")
+        f.write(f"| algorithmic FLOPs per launch (GFLOP) | {algo_flops / 1e9:.3f} |\n")
+        f.write(f"| counted / algorithmic | {flops / algo_flops:.4f} |\n")
+        f.write(f"| MfmaUtil (% of SIMD clocks with the matrix core busy) | {util:.1f} |\n")
+        f.write(f"| GRBM_GUI_ACTIVE per dispatch (clocks, summed over the 8 XCDs) | {gui:.0f} |\n")
+        f.write(f"| dispatch duration in the counter run (us) | {run_ns / 1e3:.2f} |\n")
+        f.write(f"| effective clock (GHz) | {clk / 1e9:.3f} |\n")
+        f.write(f"| kernel mean duration, kernel-trace run (us) | {us:.2f} |\n")
+        f.write(f"| algorithmic FLOP rate (TFLOP/s) | {algo_flops / (us * 1e-6) / 1e12:.1f} |\n")
+        f.write(f"| of the 2.5 PFLOP/s bf16 peak | {algo_flops / (us * 1e-6) / BF16_PEAK_FLOPS:.4f} |\n")
+        f.write(f"| of 256 CUs x 4096 FLOP/clock at the effective clock | {at_clock:.4f} |\n")
+
+
 def lookup_traffic(workload):
     """Traffic per split-K launch recorded for `workload` with the current sources, or None."""
     sha = source_sha()
@@ -132,6 +191,10 @@ def main(argv):
         return 0
     if len(argv) >= 9 and argv[0] == "traffic":
         summarize_traffic(argv[1], argv[2], argv[3], argv[4], argv[5], argv[6], int(argv[7]), argv[8])
+        print(open(argv[2]).read())
+        return 0
+    if len(argv) >= 7 and argv[0] == "mfma":
+        summarize_mfma(argv[1], argv[2], argv[3], argv[4], float(argv[5]), argv[6])
         print(open(argv[2]).read())
         return 0
     print(__doc__, file=sys.stderr)
