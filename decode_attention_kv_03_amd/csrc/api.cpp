@@ -258,8 +258,12 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   a.scale_log2 = scale * kvattn::kLog2eHost;
   a.ring_depth = KVATTN_GQA_RING_DEPTH;
   if (nsplit > 1) {
+    // Partial outputs (fp32 for an fp32 cache, bf16 otherwise), then the
+    // fp32 log-sum-exps; partial_bytes sizes the fp32 layout, which bounds both.
+    const int64_t n_part = (int64_t)batch * num_q_heads * nsplit * head_dim;
+    const size_t part_elem = cache.kind == CacheKind::kF32 ? sizeof(float) : sizeof(uint16_t);
     a.part_o = static_cast<float*>(workspace);
-    a.part_lse = a.part_o + (int64_t)batch * num_q_heads * nsplit * head_dim;
+    a.part_lse = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + n_part * part_elem);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipErrorInvalidValue;

@@ -30,7 +30,8 @@
 //    keeps its own max/sum/accumulator, merged through LDS at the end) and
 //    split the heads when it has more;
 //  * the split's result is either the final output (one split) or an fp32
-//    partial plus its log2-domain log-sum-exp for the merge kernel.
+//    partial (rounded to bf16) plus its fp32 log2-domain log-sum-exp for the
+//    merge kernel.
 #include "device_common.h"
 #include "kvattn_internal.h"
 #include "lds_copy.h"
@@ -370,9 +371,15 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
       }
       if (a.lse != nullptr && grp == 0) a.lse[row] = lse2 * kLn2;
     } else {
-      float* po = a.part_o + (row * a.n_split + split) * kHeadDim;
+      // Partial output rounded to bf16 (the merge weighs the splits in fp32
+      // from their fp32 log-sum-exps).
+      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (row * a.n_split + split) * kHeadDim;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(po + 16 * db + 4 * grp) = acc[hbi][db] * inv;
+      for (int db = 0; db < 8; ++db) {
+        const uint32_t lo = pack_bf16x2(acc[hbi][db][0] * inv, acc[hbi][db][1] * inv);
+        const uint32_t hi = pack_bf16x2(acc[hbi][db][2] * inv, acc[hbi][db][3] * inv);
+        *reinterpret_cast<uint2*>(po + 16 * db + 4 * grp) = make_uint2(lo, hi);
+      }
       if (grp == 0) a.part_lse[row * a.n_split + split] = lse2;
     }
   }

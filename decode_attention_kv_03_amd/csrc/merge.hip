@@ -7,13 +7,22 @@
 //     M = max_s lse_s,  w_s = 2^(lse_s - M),  o = sum_s w_s o_s / sum_s w_s,
 //     lse = M + log2(sum_s w_s)
 // (softmax over a union of token sets).  One wave per (sequence, head).
+// The splits of a bf16-output call (bf16 or fp8 cache) hand over bf16
+// partial outputs, those of an fp32 call fp32 ones; log-sum-exps and the
+// combination are fp32 throughout.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kvattn_internal.h"
 
 namespace kvattn {
 namespace {
 
-template <int DV, bool BF16_OUT>
+// The two bf16 values packed in a 32-bit word, widened to fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int DV, bool BF16>
 __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
   // Lane l handles float4 columns c = l % kRowLanes (+ kRowLanes * k) of
   // the splits s = l / kRowLanes + kSplitGroups * u.  Every load of a round
@@ -32,11 +41,18 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
   nv = min(nv, a.n_split);
   const int64_t row = (int64_t)b * a.num_q_heads + head;
   const float* pl = a.part_lse + row * a.n_split;
-  const float* po = a.part_o + row * a.n_split * DV;
+  // Partial outputs: four columns per load, as loaded (bf16: 8 bytes, fp32: 16).
+  using Part = std::conditional_t<BF16, uint16_t, float>;
+  using Raw = std::conditional_t<BF16, uint2, f32x4>;
+  const Part* po = reinterpret_cast<const Part*>(a.part_o) + row * a.n_split * DV;
+  auto widen = [](const Raw& w) __attribute__((always_inline)) {
+    if constexpr (BF16) return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+    else return w;
+  };
 
   // Loads of one round: splits s0 + sg + kSplitGroups * u (past the last
   // split: the last one again, weighted 0 below).
-  f32x4 x[kU][kCols];
+  Raw x[kU][kCols];
   float ls[kU];
   auto load_round = [&](int s0) {
 #pragma unroll
@@ -45,7 +61,7 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
       ls[u] = pl[s];
 #pragma unroll
       for (int k = 0; k < kCols; ++k)
-        x[u][k] = *reinterpret_cast<const f32x4*>(po + (int64_t)s * DV + 4 * (c + kRowLanes * k));
+        x[u][k] = *reinterpret_cast<const Raw*>(po + (int64_t)s * DV + 4 * (c + kRowLanes * k));
     }
   };
   if (nv > 0) load_round(0);  // in flight while the maximum and the normaliser are found
@@ -74,7 +90,7 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
       for (int u = 0; u < kU; ++u) {
         const float w = s0 + sg + kSplitGroups * u < nv ? fast_exp2(ls[u] - M) : 0.f;
 #pragma unroll
-        for (int k = 0; k < kCols; ++k) acc[k] += w * x[u][k];
+        for (int k = 0; k < kCols; ++k) acc[k] += w * widen(x[u][k]);
       }
     }
   }
@@ -90,7 +106,7 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
     for (int k = 0; k < kCols; ++k) {
       const f32x4 o4 = acc[k] * inv;
       const int64_t off = row * DV + 4 * (c + kRowLanes * k);
-      if constexpr (BF16_OUT) {
+      if constexpr (BF16) {
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
             make_uint2(pack_bf16x2(o4[0], o4[1]), pack_bf16x2(o4[2], o4[3]));
       } else {

@@ -56,8 +56,9 @@
  *    tokens that run in parallel and are combined by a log-sum-exp merge.
  *    split_tokens = 0 lets the library choose; otherwise it must be a
  *    positive multiple of KVATTN_SPLIT_ALIGN.  Results do not depend on it
- *    beyond rounding: GQA splits hand fp32 partial outputs to the merge,
- *    MLA pieces bf16 ones (their log-sum-exps and the merge stay fp32).
+ *    beyond rounding: splits hand the merge partial outputs rounded to bf16
+ *    (fp32 for an fp32 GQA call); their log-sum-exps and the merge stay
+ *    fp32.
  *    The workspace holds the per-split partial
  *    results (and, for MLA, the work plan described at kvattn_mla_decode);
  *    its size comes from the matching *_workspace_bytes() call with the same
