@@ -1,0 +1,90 @@
+"""Host logic that turns rocprofv3 output into profiles/ summaries (CPU; synthetic CSVs).
+
+The traffic summary scales each counter by what it reads for a copy of known
+size and records the kernel-source hash; bench.py looks the traffic up only
+while the sources still hash the same.  The matrix-core summary derives the
+effective clock from GRBM_GUI_ACTIVE (summed over the 8 XCDs) and the
+dispatch duration of the same run.
+"""
+
+import csv
+import os
+
+import pytest
+
+from decode_attention_kv_03_amd import profiling as P
+
+SPLIT = "void kvattn::(anonymous namespace)::gqa_split_bf16<1, 4, 2>(kvattn::DecodeArgs)"
+MERGE = "void kvattn::(anonymous namespace)::lse_merge<128, true>(kvattn::DecodeArgs)"
+COPY = "__amd_rocclr_copyBuffer"
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _counter_run(d, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, FIELDS)
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(FIELDS, r)))
+    return d
+
+
+def test_traffic_summary_scales_counters_and_round_trips_through_the_tag(tmp_path, monkeypatch):
+    # The copy of 1 GiB reads back as half its bytes on FETCH_SIZE and exactly on WRITE_SIZE.
+    copy = 1 << 30
+    cf = _counter_run(tmp_path / "cf", [(1, COPY, "FETCH_SIZE", copy / 2048, 0, 1)])
+    cw = _counter_run(tmp_path / "cw", [(1, COPY, "WRITE_SIZE", copy / 1024, 0, 1)])
+    # Two dispatches of the split kernel (mean taken), and a merge that must be ignored.
+    f = _counter_run(tmp_path / "f", [(1, SPLIT, "FETCH_SIZE", 1000.0, 0, 1), (2, SPLIT, "FETCH_SIZE", 3000.0, 0, 1),
+                                      (3, MERGE, "FETCH_SIZE", 99999.0, 0, 1)])
+    w = _counter_run(tmp_path / "w", [(1, SPLIT, "WRITE_SIZE", 10.0, 0, 1), (2, SPLIT, "WRITE_SIZE", 30.0, 0, 1)])
+    out = tmp_path / "x_traffic.md"
+    P.summarize_traffic("some_workload", str(out), str(f), str(w), str(cf), str(cw), copy, "cmd")
+    text = out.read_text()
+    assert "| HBM bytes read per launch (scaled) | 4096000 |" in text       # 2000 KiB x 1024 x 2
+    assert "| HBM bytes written per launch (scaled) | 20480 |" in text      # 20 KiB x 1024 x 1
+    assert f"source_sha={P.source_sha()}" in text
+    monkeypatch.setattr(P, "PROFILES", str(tmp_path))
+    got = P.lookup_traffic("some_workload")
+    assert got["fetch_bytes"] == 4096000 and got["write_bytes"] == 20480
+    assert P.lookup_traffic("another_workload") is None
+    # A summary taken with other sources is not reported.
+    out.write_text(text.replace(P.source_sha(), "0" * 16))
+    assert P.lookup_traffic("some_workload") is None
+
+
+def test_trace_summary_keeps_the_library_kernels(tmp_path):
+    stats = tmp_path / "run_kernel_stats.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.DictWriter(f, ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "StdDev"])
+        w.writeheader()
+        w.writerow({"Name": SPLIT, "Calls": 30, "AverageNs": 83280.0, "MinNs": 80000.0, "MaxNs": 90000.0,
+                    "StdDev": 1500.0})
+        w.writerow({"Name": "at::native::elementwise_kernel", "Calls": 5, "AverageNs": 1.0, "MinNs": 1.0,
+                    "MaxNs": 1.0, "StdDev": 0.0})
+    out = tmp_path / "t.md"
+    P.summarize_trace(str(stats), str(out), "title", "cmd")
+    text = out.read_text()
+    assert f"| `{SPLIT}` | 30 | 83.28 | 80.00 | 90.00 | 1.50 |" in text
+    assert "elementwise_kernel" not in text
+    assert P._trace_split_us(str(out)) == pytest.approx(83.28)
+
+
+def test_mfma_summary_clock_and_utilisation(tmp_path):
+    # One dispatch of 100 us during which each of the 8 XCDs counted 200,000 busy clocks (2.0 GHz).
+    us, clk, flops = 100.0, 2.0e9, 80e9
+    ns = int(us * 1e3)
+    run = _counter_run(tmp_path / "m", [(7, SPLIT, "MfmaFlopsBF16", flops, 0, ns),
+                                        (7, SPLIT, "MfmaUtil", 40.0, 0, ns),
+                                        (7, SPLIT, "GRBM_GUI_ACTIVE", 8 * clk * us * 1e-6, 0, ns)])
+    trace = tmp_path / "t.md"
+    trace.write_text(f"| `{SPLIT}` | 30 | {us:.2f} | 1 | 1 | 0 |\n")
+    out = tmp_path / "m.md"
+    P.summarize_mfma("w", str(out), str(run), str(trace), flops, "cmd")
+    text = out.read_text()
+    assert "| effective clock (GHz) | 2.000 |" in text
+    assert "| counted / algorithmic | 1.0000 |" in text
+    # 80 GFLOP in 100 us = 800 TFLOP/s: 0.32 of 2.5 PFLOP/s, and 800e12 / (256 x 4096 x 2e9) of the clock's peak
+    assert "| of the 2.5 PFLOP/s bf16 peak | 0.3200 |" in text
+    assert f"| of 256 CUs x 4096 FLOP/clock at the effective clock | {800e12 / (256 * 4096 * 2e9):.4f} |" in text
