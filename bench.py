@@ -155,26 +155,41 @@ def cpu_baseline(w, x, seconds):
     }
 
 
-def hbm_probe(torch, stream, nbytes=2 << 30):
-    """Measured read ceiling: the library's streaming-read probe over 2 GiB (beyond the 256 MB MALL)."""
+def hbm_probe(torch, stream, nbytes=2 << 30, copies=1, workgroups=(1024, 2048, 4096)):
+    """Measured read ceiling: the library's streaming-read probe, each launch reading about `nbytes` once.
+
+    By default one launch reads 2 GiB (beyond the 256 MB MALL).  With `copies` > 1 the launches
+    cycle through that many separate buffers, as the timed decode calls cycle through their input
+    copies, so a launch of a smaller size finds nothing in the last-level cache either.  For each
+    workgroup count the launch reads the largest multiple of 16 KiB per workgroup that fits in
+    `nbytes` (the probe splits its buffer evenly in 16 KiB tiles; an uneven rest would be read by a
+    single workgroup), and the rate is taken over the bytes actually read.
+    """
     from decode_attention_kv_03_amd import hbm_read_probe
 
-    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    pitch = (int(nbytes) + 4095) // 4096 * 4096
+    buf = torch.empty(copies * pitch, dtype=torch.uint8, device="cuda:0")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    best = (0.0, 0)
-    for wgs in (1024, 2048, 4096):
-        for _ in range(3):
-            hbm_read_probe(buf, wgs, sink, stream)
+    reps = max(10, copies)
+    best = (0.0, 0, 0)
+    for wgs in workgroups:
+        nb = int(nbytes) // (16384 * wgs) * (16384 * wgs)
+        if nb == 0:
+            continue
+        views = [buf[c * pitch: c * pitch + nb] for c in range(copies)]
+        for i in range(max(3, copies)):
+            hbm_read_probe(views[i % copies], wgs, sink, stream)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
-        for _ in range(10):
-            hbm_read_probe(buf, wgs, sink, stream)
+        for i in range(reps):
+            hbm_read_probe(views[i % copies], wgs, sink, stream)
         ev[1].record(stream)
         torch.cuda.synchronize()
-        gbs = 10 * nbytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
-        best = max(best, (gbs, wgs))
+        gbs = reps * nb / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+        best = max(best, (gbs, wgs, nb))
+        del views
     del buf
-    return {"gbs": round(best[0], 1), "workgroups": best[1], "bytes": nbytes,
+    return {"gbs": round(best[0], 1), "workgroups": best[1], "bytes": best[2], "copies": copies,
             "frac_of_peak": round(best[0] / HBM_PEAK_GBS, 4)}
 
 
@@ -230,6 +245,9 @@ def main():
 
     stream = torch.cuda.current_stream()
     probe = hbm_probe(torch, stream)
+    # The same probe at this call's own size: what a plain streaming read of the call's algorithmic
+    # bytes reaches here, start-up and tail included (small calls lose more of their time to both).
+    probe_same = hbm_probe(torch, stream, nbytes, copies, workgroups=(512, 1024, 2048, 4096))
     if is_gqa:
         out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=x0["q"].dtype, device=dev)
         max_len = w.seq_len
@@ -320,6 +338,8 @@ def main():
         "call_frac": round(call_gbs / HBM_PEAK_GBS, 4),
         "measured_read_ceiling_gbs": probe["gbs"],
         "frac_of_measured_ceiling": round(achieved_gbs / probe["gbs"], 4),
+        "read_probe_same_bytes_gbs": probe_same["gbs"],
+        "frac_of_read_probe_same_bytes": round(achieved_gbs / probe_same["gbs"], 4) if probe_same["gbs"] else None,
     }
     if not is_gqa:
         roofline["mfma_tflops"] = round(flops / mean_kern_s / 1e12, 1)
@@ -355,6 +375,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "hbm_read_probe": probe,
+        "hbm_read_probe_same_bytes": probe_same,
     }
     print(json.dumps(line), flush=True)
 
