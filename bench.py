@@ -155,6 +155,19 @@ def cpu_baseline(w, x, seconds):
     }
 
 
+PROBE_TILE = 16384  # bytes per tile of the streaming-read probe
+
+
+def probe_bytes(nbytes, workgroups):
+    """Bytes one probe launch reads for about `nbytes`: whole 16 KiB tiles, the same count per workgroup."""
+    return int(nbytes) // (PROBE_TILE * workgroups) * (PROBE_TILE * workgroups)
+
+
+def probe_pitch(nbytes):
+    """Distance between the probe's rotated buffers: `nbytes` rounded up to 4 KiB."""
+    return (int(nbytes) + 4095) // 4096 * 4096
+
+
 def hbm_probe(torch, stream, nbytes=2 << 30, copies=1, workgroups=(1024, 2048, 4096)):
     """Measured read ceiling: the library's streaming-read probe, each launch reading about `nbytes` once.
 
@@ -167,13 +180,13 @@ def hbm_probe(torch, stream, nbytes=2 << 30, copies=1, workgroups=(1024, 2048, 4
     """
     from decode_attention_kv_03_amd import hbm_read_probe
 
-    pitch = (int(nbytes) + 4095) // 4096 * 4096
+    pitch = probe_pitch(nbytes)
     buf = torch.empty(copies * pitch, dtype=torch.uint8, device="cuda:0")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
     reps = max(10, copies)
     best = (0.0, 0, 0)
     for wgs in workgroups:
-        nb = int(nbytes) // (16384 * wgs) * (16384 * wgs)
+        nb = probe_bytes(nbytes, wgs)
         if nb == 0:
             continue
         views = [buf[c * pitch: c * pitch + nb] for c in range(copies)]

@@ -96,3 +96,17 @@ def test_ragged_paged_and_window_accounting():
     read = 100 + 4096 * (s.batch - 1)  # 100, then 4096 for every other sequence (4096, 5000, 32768, ...)
     assert nbytes == 2 * 8 * 128 * 2 * read + 2 * s.batch * 32 * 128 * 2
     assert flops == 4 * 32 * 128 * read
+
+
+def test_probe_reads_whole_tiles_per_workgroup():
+    # The read probe splits its buffer evenly in 16 KiB tiles and leaves any rest to one workgroup;
+    # the bench therefore hands it a whole number of tiles per workgroup, never more than asked.
+    mqa = 2 * 1 * 128 * 2 * 64 * 8192 + 2 * 64 * 64 * 128 * 2  # the MQA layer's algorithmic bytes
+    assert mqa == 270_532_608
+    for wgs in (512, 1024, 2048, 4096):
+        nb = bench.probe_bytes(mqa, wgs)
+        assert nb % (16384 * wgs) == 0 and 0 < nb <= mqa and mqa - nb < 16384 * wgs
+    assert bench.probe_bytes(mqa, 512) == 256 << 20
+    assert bench.probe_bytes(2 << 30, 4096) == 2 << 30
+    assert bench.probe_bytes(1 << 20, 512) == 0  # too small for one tile per workgroup: no probe
+    assert bench.probe_pitch(4097) == 8192 and bench.probe_pitch(4096) == 4096
