@@ -14,7 +14,11 @@
 //    The copies are issued as inline assembly and awaited with explicit
 //    vmcnt counts, so the compiler never drains them before an LDS read;
 //  * rows are stored unpadded (256 B) with their 16-byte chunks XOR-swizzled
-//    by row, which keeps both LDS read patterns below conflict-free;
+//    by row, so the 16 rows of a score read and the 4 rows of each 16-lane
+//    group of a transposing read address distinct bank groups.  The hardware
+//    still reports bank-conflict stalls (SQ_LDS_BANK_CONFLICT) for about a
+//    third of this kernel's LDS-busy cycles; the LDS is busy for a small
+//    share of the kernel's time, and the stall is hidden behind the stream;
 //  * a paged cache's block-table slice for the split is staged in LDS first,
 //    so per-row block lookups never wait on the vector-memory counter;
 //  * scores are S^T = K_tile * Q^T on v_mfma_f32_16x16x32_bf16 (16 tokens x 16

@@ -19,7 +19,9 @@
 //  * tiles stream into a 2-stage LDS ring with global_load_lds_dwordx4
 //    (8 rows of one tensor per wave instruction, 32 per tile), awaited with
 //    explicit vmcnt counts; 16-byte chunks are XOR-swizzled by row so the two
-//    LDS read patterns below are conflict-free;
+//    LDS read patterns below spread over all banks (the hardware still
+//    reports bank-conflict stalls for about a third of the LDS-busy cycles,
+//    hidden behind the stream);
 //  * scores S^T = K * Q^T on v_mfma_f32_16x16x32_bf16, 16 tokens x 16 heads
 //    per product.  The 128 dims are dealt to the products so that a lane's
 //    K bytes for all four are 32 contiguous bytes of its row (two 16-byte LDS
@@ -52,8 +54,8 @@ constexpr int kRedFloatsPerWave = 34 * 64;  // 32 accumulators + max + sum, per 
 constexpr float kRescaleSlack = 8.f;        // log2 units
 
 // Chunk swizzle of a 128-byte row (8 chunks of 16 B).  Two rows share the 64
-// LDS banks, so a read is conflict-free when its rows give distinct (row
-// parity, physical chunk) pairs: 16 consecutive rows (score reads) and the
+// LDS banks, so a read spreads over all banks when its rows give distinct
+// (row parity, physical chunk) pairs: 16 consecutive rows (score reads) and the
 // rows {0-3, 16-19} + 4k (transposing reads) both do with this XOR.
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ (((row >> 4) & 1) << 2); }
 

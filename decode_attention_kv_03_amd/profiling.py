@@ -4,6 +4,7 @@
     python -m decode_attention_kv_03_amd.profiling traffic WORKLOAD OUT_MD FETCH_DIR WRITE_DIR \
         COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES COMMANDS
     python -m decode_attention_kv_03_amd.profiling mfma WORKLOAD OUT_MD RUN_DIR TRACE_MD ALGO_FLOPS COMMAND
+    python -m decode_attention_kv_03_amd.profiling lds WORKLOAD OUT_MD RUN_DIR COMMAND
 
 ``trace`` condenses a ``--kernel-trace --stats`` kernel_stats.csv into a table
 of the library's kernels.  ``traffic`` turns two ``--pmc`` runs of a workload
@@ -14,7 +15,11 @@ counters were taken with.  ``bench.py`` reports that traffic only while the
 sources still hash the same.  ``mfma`` turns one ``--pmc MfmaUtil
 MfmaFlopsBF16 GRBM_GUI_ACTIVE`` run into the split-K kernel's counted
 matrix-core FLOPs, busy fraction and effective clock, with the kernel's mean
-duration taken from its kernel-trace summary.
+duration taken from its kernel-trace summary.  ``lds`` turns one ``--pmc
+SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_INSTS_LDS
+GRBM_GUI_ACTIVE`` run into the split-K kernel's LDS bank-conflict stall
+cycles as a fraction of its LDS-busy cycles, and the share of all CU clocks
+during the dispatch in which the LDS served indexed reads and writes.
 """
 
 import csv
@@ -171,6 +176,31 @@ def summarize_mfma(workload, out_md, run_dir, trace_md, algo_flops, command):
         f.write(f"| of 256 CUs x 4096 FLOP/clock at the effective clock | {at_clock:.4f} |\n")
 
 
+def summarize_lds(workload, out_md, run_dir, command):
+    active, n = _mean_counter(run_dir, "SQ_LDS_IDX_ACTIVE", _is_split)
+    bank, _ = _mean_counter(run_dir, "SQ_LDS_BANK_CONFLICT", _is_split)
+    addr, _ = _mean_counter(run_dir, "SQ_LDS_ADDR_CONFLICT", _is_split)
+    insts, _ = _mean_counter(run_dir, "SQ_INSTS_LDS", _is_split)
+    gui, _ = _mean_counter(run_dir, "GRBM_GUI_ACTIVE", _is_split)
+    names = sorted({r["Kernel_Name"] for r in _counter_rows(run_dir) if _is_split(r["Kernel_Name"])})
+    # The SQ counters are summed over all compute units; GRBM_GUI_ACTIVE is summed over the
+    # 8 XCDs, so one XCD's busy clocks (the dispatch's clocks) are the sum / 8.
+    cu_clocks = gui / XCDS * CUS
+    with open(out_md, "w") as f:
+        f.write(f"# LDS counters of the split-K kernel: {workload}\n\n")
+        f.write("rocprofv3 counter run, from the repository root on one MI355X:\n\n")
+        f.write("```\n" + command + "\n```\n\n")
+        f.write("Kernel: " + ", ".join(f"`{k}`" for k in names) + "\n\n")
+        f.write("| quantity | value |\n|---|---|\n")
+        f.write(f"| SQ_LDS_IDX_ACTIVE per dispatch (LDS-busy cycles, all CUs; mean of {n}) | {active:.0f} |\n")
+        f.write(f"| SQ_LDS_BANK_CONFLICT per dispatch (stall cycles) | {bank:.0f} |\n")
+        f.write(f"| bank-conflict cycles / LDS-busy cycles | {bank / active:.4f} |\n")
+        f.write(f"| SQ_LDS_ADDR_CONFLICT per dispatch (stall cycles) | {addr:.0f} |\n")
+        f.write(f"| SQ_INSTS_LDS per dispatch (instructions) | {insts:.0f} |\n")
+        f.write(f"| GRBM_GUI_ACTIVE per dispatch (clocks, summed over the 8 XCDs) | {gui:.0f} |\n")
+        f.write(f"| LDS busy, share of CU clocks (SQ_LDS_IDX_ACTIVE / (256 x clocks)) | {active / cu_clocks:.4f} |\n")
+
+
 def lookup_traffic(workload):
     """Traffic per split-K launch recorded for `workload` with the current sources, or None."""
     sha = source_sha()
@@ -191,6 +221,10 @@ def main(argv):
         return 0
     if len(argv) >= 9 and argv[0] == "traffic":
         summarize_traffic(argv[1], argv[2], argv[3], argv[4], argv[5], argv[6], int(argv[7]), argv[8])
+        print(open(argv[2]).read())
+        return 0
+    if len(argv) >= 5 and argv[0] == "lds":
+        summarize_lds(argv[1], argv[2], argv[3], argv[4])
         print(open(argv[2]).read())
         return 0
     if len(argv) >= 7 and argv[0] == "mfma":

@@ -88,3 +88,21 @@ def test_mfma_summary_clock_and_utilisation(tmp_path):
     # 80 GFLOP in 100 us = 800 TFLOP/s: 0.32 of 2.5 PFLOP/s, and 800e12 / (256 x 4096 x 2e9) of the clock's peak
     assert "| of the 2.5 PFLOP/s bf16 peak | 0.3200 |" in text
     assert f"| of 256 CUs x 4096 FLOP/clock at the effective clock | {800e12 / (256 * 4096 * 2e9):.4f} |" in text
+
+
+def test_lds_summary_conflict_ratio_and_busy_share(tmp_path):
+    # One dispatch of 100 us at 2 GHz (8 XCDs x 200,000 busy clocks): 256 CUs x 200,000 = 51.2 M CU clocks,
+    # of which the LDS was busy 25.6 M (one half) and stalled on bank conflicts 256,000 (1 % of that).
+    clk = 200_000
+    run = _counter_run(tmp_path / "l", [(3, SPLIT, "SQ_LDS_IDX_ACTIVE", 25_600_000, 0, 1),
+                                        (3, SPLIT, "SQ_LDS_BANK_CONFLICT", 256_000, 0, 1),
+                                        (3, SPLIT, "SQ_LDS_ADDR_CONFLICT", 0, 0, 1),
+                                        (3, SPLIT, "SQ_INSTS_LDS", 1234, 0, 1),
+                                        (3, SPLIT, "GRBM_GUI_ACTIVE", 8 * clk, 0, 1),
+                                        (4, MERGE, "SQ_LDS_IDX_ACTIVE", 99, 0, 1)])
+    out = tmp_path / "l.md"
+    P.summarize_lds("w", str(out), str(run), "cmd")
+    text = out.read_text()
+    assert "| bank-conflict cycles / LDS-busy cycles | 0.0100 |" in text
+    assert "| LDS busy, share of CU clocks (SQ_LDS_IDX_ACTIVE / (256 x clocks)) | 0.5000 |" in text
+    assert f"`{SPLIT}`" in text and "lse_merge" not in text
