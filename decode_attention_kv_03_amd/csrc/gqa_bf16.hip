@@ -14,11 +14,9 @@
 //    The copies are issued as inline assembly and awaited with explicit
 //    vmcnt counts, so the compiler never drains them before an LDS read;
 //  * rows are stored unpadded (256 B) with their 16-byte chunks XOR-swizzled
-//    by row, so the 16 rows of a score read and the 4 rows of each 16-lane
-//    group of a transposing read address distinct bank groups.  The hardware
-//    still reports bank-conflict stalls (SQ_LDS_BANK_CONFLICT) for about a
-//    third of this kernel's LDS-busy cycles; the LDS is busy for a small
-//    share of the kernel's time, and the stall is hidden behind the stream;
+//    by row, and the score reads visit the dims in the order kchunk() below,
+//    so neither LDS read pattern stalls on bank conflicts
+//    (SQ_LDS_BANK_CONFLICT counts none for this kernel);
 //  * a paged cache's block-table slice for the split is staged in LDS first,
 //    so per-row block lookups never wait on the vector-memory counter;
 //  * scores are S^T = K_tile * Q^T on v_mfma_f32_16x16x32_bf16 (16 tokens x 16
@@ -58,6 +56,14 @@ constexpr float kRescaleSlack = 8.f;        // log2 units
 // consecutive rows 8 distinct pairs, which is what the two read patterns need.
 __device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 
+// Logical 16-byte chunk (8 dims) that lane group grp reads at score step kk.
+// The reduction over the 128 dims may visit them in any order shared by the
+// K and Q^T operands.  Giving the four lane groups chunks that differ in bits
+// 1-2 (and the steps bits 0 and 3) keeps lanes l and l+16, which read the
+// same row, off the banks that the XOR with swz() aligns across rows r and
+// r+8; the order 4*kk + grp measured 4 bank-conflict cycles per score read.
+__device__ __forceinline__ int kchunk(int kk, int grp) { return (kk & 1) | (grp << 1) | ((kk >> 1) << 3); }
+
 template <int HBW, int WH, int NST>
 __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeArgs a) {
   static_assert(WH == 1 || HBW == 1, "token-split waves own one head block");
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
   const int hb0 = (wave / WH) * HBW;  // first 16-head block of this wave
   const int ts = wave % WH;           // this wave's token slot within a tile
 
-  // Q^T fragments: lane l holds head (block*16 + l%16), dims 32*kk + 8*(l/16) .. +7.
+  // Q^T fragments: lane l holds head (block*16 + l%16), dims 8*kchunk(kk, l/16) .. +7.
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * h + (int64_t)j * r) * kHeadDim;
   bf16x8 qf[HBW][4];
 #pragma unroll
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < r) v = *reinterpret_cast<const u32x4*>(qg + head * kHeadDim + 32 * kk + 8 * grp);
+      if (head < r) v = *reinterpret_cast<const u32x4*>(qg + head * kHeadDim + 8 * kchunk(kk, grp));
       qf[hbi][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -218,12 +224,12 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
   };
 
   // Per-lane LDS byte offsets inside a tile.  K reads (A operand of the
-  // scores): row n16 of a 16-token subtile, chunk 4*kk + grp.  V transposing
+  // scores): row n16 of a 16-token subtile, chunk kchunk(kk, grp).  V transposing
   // reads: rows 4*grp + (n16/4) (+16 per subtile), 8-byte piece n16%4 of the
   // 16-column block db, i.e. chunk 2*db + (n16%4)/2.
   int koff[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) koff[kk] = n16 * kRowB + 16 * ((4 * kk + grp) ^ swz(n16));
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = n16 * kRowB + 16 * (kchunk(kk, grp) ^ swz(n16));
   const int vrow = 4 * grp + (n16 >> 2);
   int voff[8];
 #pragma unroll
