@@ -18,14 +18,13 @@
 // and walks it in 128-token tiles (128 B per row, 16 KiB per tensor and tile):
 //  * tiles stream into a 2-stage LDS ring with global_load_lds_dwordx4
 //    (8 rows of one tensor per wave instruction, 32 per tile), awaited with
-//    explicit vmcnt counts; 16-byte chunks are XOR-swizzled by row so the two
-//    LDS read patterns below spread over all banks (the hardware still
-//    reports bank-conflict stalls for about a third of the LDS-busy cycles,
-//    hidden behind the stream);
+//    explicit vmcnt counts; 16-byte chunks are XOR-swizzled by row, and the
+//    score reads take their chunks in an order (below) under which neither
+//    LDS read pattern stalls on bank conflicts;
 //  * scores S^T = K * Q^T on v_mfma_f32_16x16x32_bf16, 16 tokens x 16 heads
 //    per product.  The 128 dims are dealt to the products so that a lane's
-//    K bytes for all four are 32 contiguous bytes of its row (two 16-byte LDS
-//    reads), with the query fragments dealt the same way;
+//    K bytes for all four are two 16-byte chunks of its row (two LDS reads),
+//    with the query fragments dealt the same way;
 //  * O^T += V^T * P^T, 32 tokens per product: V^T comes straight from the
 //    row-major tile through the gfx950 8-bit transposing read
 //    (ds_read_b64_tr_b8), whose lanes address the eight token rows the
@@ -111,7 +110,8 @@ __global__ __launch_bounds__(256, 2) void gqa_split_fp8(DecodeArgs a) {
   const float v_sc = a.v_scale[j];
 
   // Q^T fragments.  Product kk of a score takes, in lane group grp, the dims
-  // 32*grp + 8*kk .. +7 (the K fragment below takes the same dims).
+  // 64*(kk/2) + 16*grp + 8*(kk%2) .. +7 (the K fragment below takes the same
+  // dims).
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + ((int64_t)b * h + (int64_t)j * r) * kHeadDim;
   bf16x8 qf[HBW][4];
 #pragma unroll
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void gqa_split_fp8(DecodeArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (head < r) v = *reinterpret_cast<const u32x4*>(qg + head * kHeadDim + 32 * grp + 8 * kk);
+      if (head < r) v = *reinterpret_cast<const u32x4*>(qg + head * kHeadDim + 64 * (kk >> 1) + 16 * grp + 8 * (kk & 1));
       qf[hbi][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -229,8 +229,12 @@ __global__ __launch_bounds__(256, 2) void gqa_split_fp8(DecodeArgs a) {
   };
 
   // Per-lane LDS byte offsets inside a 32-token unit.  Score reads (A
-  // operand): row 16*sb + n16, logical chunks 2*grp and 2*grp + 1 (dims
-  // 32*grp .. +31); the swizzle of rows 16..31 differs from 0..15.
+  // operand): row 16*sb + n16, logical chunks grp and 4 + grp (dims 16*grp
+  // .. +15 and 64 + 16*grp .. +15); the swizzle of rows 16..31 differs from
+  // 0..15.  The order 2*grp + c measured 4 bank-conflict cycles per read: the
+  // four lane groups read the same 16 rows, and chunks 2*grp + c put pairs of
+  // groups on the banks that the XOR with swz() aligns across rows; chunks
+  // 4*c + grp do not.
   // Transposing V reads: lane n16 of group grp addresses token row
   // R(grp, n16/2), R(grp, v) = 4*grp + v for v < 4 and 16 + 4*grp + v-4
   // otherwise, bytes 16*db + 8*(n16%2) .. +7; it then holds column
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void gqa_split_fp8(DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int row = 16 * sb + n16;
-      koff[sb][c] = row * kRowB + 16 * ((2 * grp + c) ^ swz(row));
+      koff[sb][c] = row * kRowB + 16 * ((4 * c + grp) ^ swz(row));
     }
   const int vv = n16 >> 1;
   const int vrow = (vv & 3) + 4 * grp + 16 * (vv >> 2);
