@@ -12,6 +12,7 @@
 #include <string>
 
 #include "../../include/kvattn.h"
+#include "../../include/kvattn_measure.h"
 #include "kvattn_internal.h"
 
 namespace {
@@ -40,11 +41,10 @@ kvattn_status ok() {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-#ifndef KVATTN_GQA_RING_DEPTH
-#define KVATTN_GQA_RING_DEPTH 2
-#endif
-
 constexpr int kCUs = 256;          // MI355X compute units
+// Longest sequence a call takes: token indices, split ends and piece ends stay
+// well inside 32-bit arithmetic on the device.
+constexpr int32_t kMaxSeqLen = 1 << 28;
 constexpr int32_t kMaxGridYZ = 65535;  // largest y/z grid dimension the launches use
 
 // Tokens per split for GQA.  A contiguous cache is taken to hold sequences of
@@ -54,8 +54,9 @@ constexpr int32_t kMaxGridYZ = 65535;  // largest y/z grid dimension the launche
 // is taken to hold ragged lengths: about four workgroups per CU in all, each
 // at most 2048 tokens, so that long sequences do not leave a tail.
 int32_t plan_gqa_split(int32_t batch, int32_t h, int32_t g, int32_t max_seq_len, bool paged, int32_t requested) {
-  if (requested > 0) return requested;
   const int64_t S = max_seq_len > 0 ? max_seq_len : 1;
+  // A requested split longer than the longest sequence is one split either way.
+  if (requested > 0) return (int32_t)std::min<int64_t>(requested, round_up(S, KVATTN_SPLIT_ALIGN));
   const int64_t units = (int64_t)batch * g;
   const int64_t r = h / g;
   const int64_t min_chunk = std::max<int64_t>(256, 16 * r);
@@ -112,7 +113,7 @@ MlaWorkspace mla_workspace(int64_t batch, int64_t heads, int64_t max_pieces, int
 
 int32_t n_splits(int32_t max_seq_len, int32_t split) {
   if (max_seq_len <= split) return 1;
-  return (int32_t)((max_seq_len + split - 1) / split);
+  return (int32_t)(((int64_t)max_seq_len + split - 1) / split);
 }
 
 size_t partial_bytes(int64_t batch, int64_t heads, int64_t nsplit, int64_t d_v) {
@@ -137,6 +138,8 @@ int32_t pow2_shift(int32_t x) {
 kvattn_status check_cache_geometry(int64_t cache_len, int32_t block_size, int32_t max_blocks, int32_t max_seq_len,
                                    bool paged) {
   if (max_seq_len < 0) return fail(KVATTN_ERR_INVALID, "max_seq_len must be >= 0 (got %lld)", max_seq_len);
+  if (max_seq_len > kMaxSeqLen)
+    return fail(KVATTN_ERR_UNSUPPORTED, "max_seq_len %lld exceeds the supported %lld tokens", max_seq_len, kMaxSeqLen);
   if (cache_len < 1) return fail(KVATTN_ERR_INVALID, "cache_len must be >= 1 (got %lld)", cache_len);
   if (!paged) {
     if (max_seq_len > cache_len)
@@ -220,14 +223,24 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
     return st;
   if ((st = check_split(split_tokens)) != KVATTN_OK) return st;
 
-  // A window needs only the tokens from the 64-aligned token below its start:
-  // at most window + 63 per sequence.  Splits are planned for that span (the
-  // planners give no more splits for a shorter span, so the workspace query
-  // for the full context still bounds this call's needs; the check below
-  // guards it).
-  const int32_t span = window > 0 ? (int32_t)std::min<int64_t>(max_seq_len, (int64_t)window + 63) : max_seq_len;
-  const int32_t split = plan_gqa_split(batch, num_q_heads, num_kv_heads, span, paged, split_tokens);
-  const int32_t nsplit = n_splits(span, split);
+  // Splits.  A window needs only the tokens from the 64-aligned token below
+  // its start, at most window + 63 per sequence, so its splits are planned on
+  // that span.  The automatic plan is not monotone in the span (a shorter
+  // span can get more splits), so a window call never takes more splits than
+  // the whole context would: the workspace kvattn_gqa_workspace_bytes reports
+  // (it takes no window) then always suffices.
+  const int32_t full_split = plan_gqa_split(batch, num_q_heads, num_kv_heads, max_seq_len, paged, split_tokens);
+  const int32_t full_n = n_splits(max_seq_len, full_split);
+  int32_t split = full_split, nsplit = full_n;
+  if (window > 0) {
+    const int32_t span = (int32_t)std::min<int64_t>(max_seq_len, (int64_t)window + 63);
+    split = plan_gqa_split(batch, num_q_heads, num_kv_heads, span, paged, split_tokens);
+    nsplit = n_splits(span, split);
+    if (nsplit > full_n) {
+      split = (int32_t)round_up((span + full_n - 1) / full_n, KVATTN_SPLIT_ALIGN);
+      nsplit = n_splits(span, split);
+    }
+  }
   const size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
@@ -256,7 +269,6 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   a.split_tokens = split;
   a.n_split = nsplit;
   a.scale_log2 = scale * kvattn::kLog2eHost;
-  a.ring_depth = KVATTN_GQA_RING_DEPTH;
   if (nsplit > 1) {
     // Partial outputs (fp32 for an fp32 cache, bf16 otherwise), then the
     // fp32 log-sum-exps; partial_bytes sizes the fp32 layout, which bounds both.
@@ -274,7 +286,7 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   }
   if (e != hipSuccess) return hip_status(e, "split kernel launch");
   if (nsplit > 1) {
-    e = kvattn::launch_merge(a, head_dim, cache.kind != CacheKind::kF32, s);
+    e = kvattn::launch_merge(a, cache.kind != CacheKind::kF32, s);
     if (e != hipSuccess) return hip_status(e, "merge kernel launch");
   }
   return ok();
@@ -299,7 +311,7 @@ const char* kvattn_last_error(void) { return g_last_error.c_str(); }
 
 int32_t kvattn_gqa_split_tokens(int32_t batch, int32_t h, int32_t g, int32_t max_seq_len, int32_t block_size,
                                 int32_t split_tokens) {
-  if (batch < 1 || h < 1 || g < 1 || h % g != 0 || split_tokens < 0) return -1;
+  if (batch < 1 || h < 1 || g < 1 || h % g != 0 || split_tokens < 0 || max_seq_len > kMaxSeqLen) return -1;
   return plan_gqa_split(batch, h, g, max_seq_len, block_size > 0, split_tokens);
 }
 
@@ -313,8 +325,8 @@ int32_t kvattn_mla_split_tokens(int32_t batch, int32_t h, int32_t max_seq_len, i
 size_t kvattn_gqa_workspace_bytes(int32_t batch, int32_t h, int32_t g, int32_t d, int32_t max_seq_len,
                                   int32_t block_size, int32_t split_tokens, kvattn_dtype dtype) {
   (void)dtype;
-  if (batch < 1 || h < 1 || g < 1 || h % g != 0 || d < 1 || max_seq_len < 0 || split_tokens < 0 ||
-      split_tokens % KVATTN_SPLIT_ALIGN != 0)
+  if (batch < 1 || h < 1 || g < 1 || h % g != 0 || d < 1 || max_seq_len < 0 || max_seq_len > kMaxSeqLen ||
+      split_tokens < 0 || split_tokens % KVATTN_SPLIT_ALIGN != 0)
     return (size_t)-1;
   const int32_t split = plan_gqa_split(batch, h, g, max_seq_len, block_size > 0, split_tokens);
   return partial_bytes(batch, h, n_splits(max_seq_len, split), d);
@@ -325,7 +337,8 @@ size_t kvattn_mla_workspace_bytes(int32_t batch, int32_t h, int32_t d_c, int32_t
   (void)dtype;
   (void)d_r;
   (void)block_size;
-  if (batch < 1 || h < 1 || d_c < 1 || max_seq_len < 0 || split_tokens < 0 || split_tokens % KVATTN_SPLIT_ALIGN != 0)
+  if (batch < 1 || h < 1 || d_c < 1 || max_seq_len < 0 || max_seq_len > kMaxSeqLen || split_tokens < 0 ||
+      split_tokens % KVATTN_SPLIT_ALIGN != 0)
     return (size_t)-1;
   const int64_t max_pieces = mla_max_pieces(batch, max_seq_len, split_tokens);
   if (max_pieces < 0) return (size_t)-1;

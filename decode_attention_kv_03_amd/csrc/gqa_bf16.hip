@@ -8,9 +8,9 @@
 //
 // Work decomposition.  One workgroup (4 waves) owns one (sequence, KV head,
 // split) and walks the split's tokens in 64-token tiles:
-//  * tiles stream from HBM straight into an NST-stage LDS ring with
+//  * tiles stream from HBM straight into a two-stage LDS ring with
 //    global_load_lds_dwordx4 carrying the non-temporal hint (the cache is
-//    read once per step); NST-1 tiles are in flight while one is consumed.
+//    read once per step); one tile is in flight while the other is consumed.
 //    The copies are issued as inline assembly and awaited with explicit
 //    vmcnt counts, so the compiler never drains them before an LDS read;
 //  * rows are stored unpadded (256 B) with their 16-byte chunks XOR-swizzled
@@ -34,6 +34,8 @@
 //  * the split's result is either the final output (one split) or an fp32
 //    partial (rounded to bf16) plus its fp32 log2-domain log-sum-exp for the
 //    merge kernel.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "kvattn_internal.h"
 #include "lds_copy.h"
@@ -64,10 +66,10 @@ __device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >>
 // r+8; the order 4*kk + grp measured 4 bank-conflict cycles per score read.
 __device__ __forceinline__ int kchunk(int kk, int grp) { return (kk & 1) | (grp << 1) | ((kk >> 1) << 3); }
 
-template <int HBW, int WH, int NST>
-__global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeArgs a) {
+template <int HBW, int WH>
+__global__ __launch_bounds__(256, 2) void gqa_split_bf16(DecodeArgs a) {
   static_assert(WH == 1 || HBW == 1, "token-split waves own one head block");
-  static_assert(NST >= 2 && NST <= 3, "ring depth");
+  constexpr int NST = 2;  // LDS ring stages
   constexpr int kUnit = WH == 4 ? 16 : 32;  // tokens a wave handles per step
   // 1-D grid, XCD-aware: workgroup w runs on XCD w % 8 and all splits of one
   // (sequence, KV head) group share a residue, so the group's queries are
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
   for (int db = 0; db < 8; ++db)
     voff[db] = kTileB + vrow * kRowB + 16 * ((2 * db + ((n16 & 3) >> 1)) ^ swz(vrow)) + 8 * (n16 & 1);
 
-  for (int s = 0; s < NST - 1 && s < n_tiles; ++s) issue_tile(t_begin + s * kTile, s);
+  if (n_tiles > 0) issue_tile(t_begin, 0);
   // The queries and the first tiles were fetched together (one HBM latency at
   // start-up, not two).  Let them all land here: the compiler cannot see the
   // copies in the vector-memory counter, and a wait it placed on the query
@@ -244,12 +246,10 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   for (int it = 0; it < n_tiles; ++it) {
-    // Tile `it` must have landed; the ones issued after it may stay in flight.
-    const int ahead = min(NST - 2, n_tiles - 1 - it);
-    if (ahead >= 2) wait_copies_and_sync<16>();
-    else if (ahead == 1) wait_copies_and_sync<8>();
-    else wait_copies_and_sync<0>();
-    if (it + NST - 1 < n_tiles) issue_tile(t_begin + (it + NST - 1) * kTile, (it + NST - 1) % NST);
+    // Tile `it` must have landed (nothing else is in flight here); then the
+    // next tile's copies go into the other stage, which every wave is done with.
+    wait_copies_and_sync<0>();
+    if (it + 1 < n_tiles) issue_tile(t_begin + (it + 1) * kTile, (it + 1) % NST);
 
     const int t0 = t_begin + it * kTile;
     const unsigned char* stage = ring[it % NST];
@@ -395,30 +395,25 @@ __global__ __launch_bounds__(256, NST == 2 ? 2 : 1) void gqa_split_bf16(DecodeAr
   }
 }
 
-template <int NST>
-hipError_t launch_depth(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
+}  // namespace
+
+hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
   const int64_t units = (int64_t)a.batch * a.num_kv_heads;
   const dim3 grid((unsigned)(8 * ((units + 7) / 8) * a.n_split));
   const dim3 block(256);
   const int head_blocks = (a.group + 15) / 16;
   if (head_blocks == 1) {
-    hipExtLaunchKernelGGL((gqa_split_bf16<1, 4, NST>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((gqa_split_bf16<1, 4>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
   } else if (head_blocks == 2) {
-    hipExtLaunchKernelGGL((gqa_split_bf16<1, 2, NST>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((gqa_split_bf16<1, 2>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
   } else if (head_blocks <= 4) {
-    hipExtLaunchKernelGGL((gqa_split_bf16<1, 1, NST>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((gqa_split_bf16<1, 1>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
   } else if (head_blocks <= 8) {
-    hipExtLaunchKernelGGL((gqa_split_bf16<2, 1, NST>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((gqa_split_bf16<2, 1>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-}  // namespace
-
-hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
-  return a.ring_depth == 3 ? launch_depth<3>(a, stream, ev) : launch_depth<2>(a, stream, ev);
 }
 
 }  // namespace kvattn

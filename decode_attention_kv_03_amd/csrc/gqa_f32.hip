@@ -14,6 +14,8 @@
 //  4. one thread per (head, pair of output columns) rescales its running
 //     output and adds the tile's probability-weighted V rows.
 #include "cache_addr.h"
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "kvattn_internal.h"
 

@@ -31,6 +31,8 @@
 //    probability operand holds;
 //  * online softmax, lazy rescaling, head blocks, wave token slots and the
 //    split output are those of the bf16 kernel.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "kvattn_internal.h"
 #include "lds_copy.h"

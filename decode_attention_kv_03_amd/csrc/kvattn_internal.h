@@ -1,7 +1,6 @@
 // Host <-> kernel interface of libkvattn (not part of the public C ABI).
 #pragma once
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -48,7 +47,6 @@ struct DecodeArgs {
   int32_t split_tokens;     // tokens per split (multiple of 64)
   int32_t n_split;          // splits per sequence in the grid
   float scale_log2;         // softmax scale * log2(e): scores are kept in log2 units
-  int32_t ring_depth;       // bf16 GQA: LDS ring stages (2 or 3)
   // MLA work plan, written on the device by the plan kernel:
   //   pieces[q] = (sequence, first token, end token, 1 if it is the sequence's only piece)
   //   seq_pieces[b] = (first piece, number of pieces); plan_count = {pieces, piece length}
@@ -85,7 +83,7 @@ hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream, const Launch
 hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t stream);
 hipError_t launch_mla_merge_pieces(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_hbm_read_probe(const void* buf, int64_t n16, uint32_t* sink, int workgroups, hipStream_t stream);
-// Log-sum-exp merge of the per-split partials into out/lse; d_v = 128 or 512.
-hipError_t launch_merge(const DecodeArgs& a, int d_v, bool out_bf16, hipStream_t stream);
+// Log-sum-exp merge of the per-split GQA partials into out/lse (d_v = 128).
+hipError_t launch_merge(const DecodeArgs& a, bool out_bf16, hipStream_t stream);
 
 }  // namespace kvattn

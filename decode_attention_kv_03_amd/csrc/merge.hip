@@ -119,18 +119,11 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_merge(const DecodeArgs& a, int d_v, bool out_bf16, hipStream_t stream) {
+hipError_t launch_merge(const DecodeArgs& a, bool out_bf16, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.batch);
   const dim3 block(64);
-  if (d_v == kHeadDim) {
-    if (out_bf16) lse_merge<kHeadDim, true><<<grid, block, 0, stream>>>(a);
-    else lse_merge<kHeadDim, false><<<grid, block, 0, stream>>>(a);
-  } else if (d_v == kMlaLatent) {
-    if (out_bf16) lse_merge<kMlaLatent, true><<<grid, block, 0, stream>>>(a);
-    else lse_merge<kMlaLatent, false><<<grid, block, 0, stream>>>(a);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (out_bf16) lse_merge<kHeadDim, true><<<grid, block, 0, stream>>>(a);
+  else lse_merge<kHeadDim, false><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -44,6 +44,8 @@
 // probabilities stay below 2^8, exact in the fp32 accumulators and
 // representable in bf16.  The value product reduces over tokens in the same
 // per-lane order the scores come out in, so P^T needs no data movement.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "kvattn_internal.h"
 #include "lds_copy.h"
@@ -68,14 +70,8 @@ constexpr int kSteps = kMlaRow / 16 / 2;       // 18 score reduction steps per w
 constexpr int kColBlocks = kMlaLatent / 32 / 2;  // 8 output column blocks per wave
 constexpr int kSxFloats = kWaves * 16 * 64;    // partial-score exchange: 16 floats per lane
 constexpr float kRescaleSlack = 8.f;           // log2 units
-#ifndef MLA_KDEPTH
-#define MLA_KDEPTH 3
-#endif
-#ifndef MLA_VDEPTH
-#define MLA_VDEPTH 3
-#endif
-constexpr int kKDepth = MLA_KDEPTH;            // LDS operand reads in flight, score product
-constexpr int kVDepth = MLA_VDEPTH;            // ... and value product
+constexpr int kKDepth = 3;                     // LDS operand reads in flight, score product
+constexpr int kVDepth = 3;                     // ... and value product
 
 // LDS byte offset of 16-byte chunk `chunk` (0..71) of tile row `row` (0..31).
 __device__ __forceinline__ int lds_chunk(int row, int chunk) {

@@ -119,15 +119,21 @@ def _randn(shape, gen, device, dtype, chunks=1):
     return out
 
 
-def ragged_lengths_and_table(batch, max_len, block_size, seed):
+def ragged_lengths_and_table(batch, max_len, block_size, seed, lens=None):
     """Paged-cache structure: lengths uniform on {1..max_len}, then a random permutation of physical blocks.
 
     Logical blocks are enumerated sequence by sequence; sequence ``b``'s k-th
-    block is ``perm[offset_b + k]``; unused table entries are -1.  Returns
-    (lens int32 [B], table int32 [B, ceil(max_len/block_size)], num_blocks).
+    block is ``perm[offset_b + k]``; unused table entries are -1.  ``lens``
+    fixes the lengths instead of drawing them (the permutation is still
+    drawn).  Returns (lens int32 [B], table int32 [B, ceil(max_len/block_size)],
+    num_blocks).
     """
     rng = np.random.default_rng(seed)
-    lens = rng.integers(1, max_len + 1, size=batch)
+    if lens is None:
+        lens = rng.integers(1, max_len + 1, size=batch)
+    else:
+        lens = np.asarray(lens, dtype=np.int64)
+        assert lens.shape == (batch,) and lens.min() >= 0 and lens.max() <= max_len
     nblk = (lens + block_size - 1) // block_size
     num_blocks = int(nblk.sum())
     perm = rng.permutation(num_blocks)
@@ -145,8 +151,9 @@ def make_gqa_inputs(w, device="cpu", lens=None, poison_tail=False):
 
     Returns a dict with q [B,h,d], k, v (contiguous [B,g,S,d] or pool
     [N,g,bs,d]), seq_lens int32 [B], block_table int32 [B, max_blocks] or
-    None, all on ``device``.  ``lens`` overrides the per-sequence lengths of a
-    contiguous cache (default: every sequence is full).  With
+    None, all on ``device``.  ``lens`` overrides the per-sequence lengths
+    (default: every sequence of a contiguous cache is full; a paged cache
+    draws them uniformly on {1..seq_len}).  With
     ``poison_tail`` every cache slot past a sequence's length holds NaN.
     """
     gen = torch.Generator(device=device).manual_seed(w.seed)
@@ -162,7 +169,8 @@ def make_gqa_inputs(w, device="cpu", lens=None, poison_tail=False):
         return _fp8_codes(shape, gen, device, scales, 1, chunks) if fp8 else _randn(shape, gen, device, dt, chunks)
 
     if w.paged:
-        lens_np, table, N = ragged_lengths_and_table(B, w.seq_len, w.block_size, w.seed)
+        lens_np, table, N = ragged_lengths_and_table(B, w.seq_len, w.block_size, w.seed, lens)
+        N = max(N, 1)
         k = cache((N, g, w.block_size, d), 16, k_scale if fp8 else None)
         v = cache((N, g, w.block_size, d), 16, v_scale if fp8 else None)
         bt = torch.from_numpy(table).to(device)
@@ -193,7 +201,8 @@ def make_mla_inputs(w, device="cpu", lens=None, poison_tail=False):
     B, h, width = w.batch, w.num_heads, w.d_latent + w.d_rope
     q = _randn((B, h, width), gen, device, dt)
     if w.paged:
-        lens_np, table, N = ragged_lengths_and_table(B, w.seq_len, w.block_size, w.seed)
+        lens_np, table, N = ragged_lengths_and_table(B, w.seq_len, w.block_size, w.seed, lens)
+        N = max(N, 1)
         cache = _randn((N, w.block_size, width), gen, device, dt, chunks=16)
         bt = torch.from_numpy(table).to(device)
     else:

@@ -47,8 +47,11 @@
  *    sequence uses lie in [0, num_blocks).  The kernels never read out of
  *    bounds when they are violated: lengths are clamped to [0, max_seq_len]
  *    and to the cache capacity, and a token whose table entry is out of
- *    range is read from an in-bounds stand-in (zeros for GQA, row 0 of the
- *    pool for MLA); its contribution is then unspecified.
+ *    range is read from an in-bounds stand-in row instead (zeros in the fp32
+ *    GQA kernel; the pool's first rows in the bf16 and fp8 GQA kernels and in
+ *    MLA), which still takes part in that sequence's softmax.  That
+ *    sequence's output is then unspecified (but finite for finite cache
+ *    contents); no other sequence's output is affected.
  *  - A sequence with length 0 gets out = 0 and lse = -inf.
  *  - Accumulation is fp32 for every input dtype.  `out` has the input dtype
  *    (rounded to nearest even for bf16); `lse` is fp32, natural log.
@@ -237,30 +240,6 @@ int32_t kvattn_gqa_split_tokens(int32_t batch, int32_t num_q_heads, int32_t num_
                                 int32_t max_seq_len, int32_t block_size, int32_t split_tokens);
 int32_t kvattn_mla_split_tokens(int32_t batch, int32_t num_heads, int32_t max_seq_len,
                                 int32_t block_size, int32_t split_tokens);
-
-/*
- * Measurement utility: the next decode call (any kvattn_*_decode* entry point)
- * made on the calling thread records `start_event` when its split-K kernel
- * (the kernel that reads the cache) starts executing and `stop_event` when it
- * ends, so the caller can time that kernel alone with hipEventElapsedTime.
- * Both are hipEvent_t handles the caller created with timing enabled (both
- * non-NULL, or both NULL to disarm).  The setting is consumed by that next
- * call whether or not it succeeds; the log-sum-exp merge kernel the call may
- * add afterwards, and the MLA plan kernel before it, are outside the two
- * events.
- */
-kvattn_status kvattn_time_next_kernel(void* start_event, void* stop_event);
-
-/*
- * Measurement utility, not part of the attention path: stream `bytes` bytes
- * of device memory at `buf` through 16-byte loads with `workgroups`
- * workgroups of 256 threads, to measure the device's practical HBM read
- * bandwidth (time it with events on `stream`).  `bytes` must be a positive
- * multiple of 16 and `buf` 16-byte aligned; `sink` is a device uint32 the
- * kernel may write (it keeps the loads from being optimised away).
- */
-kvattn_status kvattn_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,
-                                    void* stream);
 
 /* Static description of a status code. */
 const char* kvattn_status_string(kvattn_status status);

@@ -1,0 +1,173 @@
+// Host-side checks of libkvattn's C ABI, built from api.cpp with the launcher
+// stand-ins of stub_launch.cpp (no GPU, no kernel code) so that the argument
+// checks, the split planning and the workspace layout run under the address
+// and undefined-behaviour sanitizers.  Prints one line per failed check and
+// exits non-zero if any failed.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+
+#include "../../include/kvattn.h"
+#include "stub_launch.h"
+
+static int g_failed = 0, g_checked = 0;
+#define CHECK(cond, ...)                                  \
+  do {                                                    \
+    ++g_checked;                                          \
+    if (!(cond)) {                                        \
+      ++g_failed;                                         \
+      std::printf("FAILED %s:%d: %s  ", __FILE__, __LINE__, #cond); \
+      std::printf(__VA_ARGS__);                           \
+      std::printf("\n");                                  \
+    }                                                     \
+  } while (0)
+
+static void* const P = reinterpret_cast<void*>(16);  // never dereferenced: no kernel runs
+static const int32_t* const PI = reinterpret_cast<const int32_t*>(16);
+static const size_t kRejected = (size_t)-1;
+
+static kvattn_status gqa_window(int32_t B, int32_t h, int32_t g, int32_t S, int32_t bs, int32_t window, int32_t split,
+                                size_t ws, kvattn_dtype dt = KVATTN_BF16) {
+  const bool paged = bs > 0;
+  const int32_t maxb = paged ? (S + bs - 1) / bs : 0;
+  const int64_t cache_len = paged ? (int64_t)B * maxb : (S > 0 ? S : 1);
+  return kvattn_gqa_decode_window(P, P, P, paged ? PI : nullptr, PI, P, nullptr, B, h, g, 128, cache_len, bs, maxb, S,
+                                  0.1f, window, dt, split, ws ? P : nullptr, ws, nullptr);
+}
+
+static void window_sweep() {
+  // A window call accepts exactly the bytes kvattn_gqa_workspace_bytes reports for the same arguments
+  // (the query takes no window), and its splits cover the window's span.
+  const int32_t Ss[] = {1, 64, 100, 1000, 2112, 4096, 8192, 32768, 65536};
+  const int32_t Ws[] = {1, 63, 64, 100, 1730, 4096, 8191, 40000};
+  const int32_t Bs[] = {1, 8, 64};
+  const int32_t HG[][2] = {{8, 8}, {32, 8}, {64, 8}, {64, 1}, {128, 1}};
+  const int32_t BSs[] = {0, 16, 1, 5};
+  const int32_t splits[] = {0, 64, 1024};
+  for (int32_t S : Ss)
+    for (int32_t W : Ws)
+      for (int32_t B : Bs)
+        for (auto& hg : HG)
+          for (int32_t bs : BSs)
+            for (int32_t split : splits) {
+              const size_t ws = kvattn_gqa_workspace_bytes(B, hg[0], hg[1], 128, S, bs, split, KVATTN_BF16);
+              CHECK(ws != kRejected, "S=%d", S);
+              stub::last = stub::Record{};
+              const kvattn_status st = gqa_window(B, hg[0], hg[1], S, bs, W, split, ws);
+              CHECK(st == KVATTN_OK, "S=%d W=%d B=%d h=%d g=%d bs=%d split=%d ws=%zu: %s", S, W, B, hg[0], hg[1], bs,
+                    split, ws, kvattn_last_error());
+              if (st != KVATTN_OK) continue;
+              const kvattn::DecodeArgs& a = stub::last.args;
+              const int64_t span = W < S ? (int64_t)W + 63 < S ? W + 63 : S : S;
+              CHECK(a.split_tokens > 0 && a.split_tokens % 64 == 0, "split %d", a.split_tokens);
+              CHECK((int64_t)a.n_split * a.split_tokens >= span, "S=%d W=%d: %d x %d < %lld", S, W, a.n_split,
+                    a.split_tokens, (long long)span);
+              CHECK(a.n_split == 1 || (int64_t)(a.n_split - 1) * a.split_tokens < span, "empty split");
+              const size_t need = a.n_split > 1 ? (size_t)B * hg[0] * a.n_split * 129 * 4 : 0;
+              CHECK(need <= ws, "need %zu > queried %zu", need, ws);
+              CHECK(stub::last.merges == (a.n_split > 1 ? 1 : 0), "merge count");
+            }
+}
+
+static void gqa_rejections() {
+  CHECK(gqa_window(2, 8, 3, 64, 0, 0, 0, 0) == KVATTN_ERR_INVALID, "h %% g");
+  CHECK(gqa_window(2, 8, 2, 64, 0, -1, 0, 0) == KVATTN_ERR_INVALID, "negative window");
+  CHECK(gqa_window(2, 8, 2, 64, 0, 0, 100, 0) == KVATTN_ERR_INVALID, "split not a multiple of 64");
+  CHECK(gqa_window(0, 8, 2, 64, 0, 0, 0, 0) == KVATTN_ERR_INVALID, "batch 0");
+  CHECK(gqa_window(2, 256, 1, 64, 0, 0, 0, 0) == KVATTN_ERR_UNSUPPORTED, "group 256");
+  CHECK(gqa_window(2, 128, 1, 64, 0, 0, 0, 0, KVATTN_F32) == KVATTN_ERR_UNSUPPORTED, "fp32 group 128");
+  const size_t need = kvattn_gqa_workspace_bytes(2, 8, 2, 128, 4096, 0, 256, KVATTN_BF16);
+  CHECK(need == (size_t)2 * 8 * 16 * 129 * 4, "need %zu", need);
+  CHECK(gqa_window(2, 8, 2, 4096, 0, 0, 256, need - 1) == KVATTN_ERR_WORKSPACE, "short workspace");
+  CHECK(gqa_window(2, 8, 2, 4096, 0, 0, 256, need) == KVATTN_OK, "%s", kvattn_last_error());
+}
+
+static void mla_sweep() {
+  const int32_t Bs[] = {1, 5, 32, 300, 600, 5000};
+  const int32_t Ss[] = {1, 100, 8192, 65536};
+  const int32_t splits[] = {0, 64, 1024};
+  const int32_t bss[] = {0, 64, 1};
+  for (int32_t B : Bs)
+    for (int32_t S : Ss)
+      for (int32_t split : splits)
+        for (int32_t bs : bss) {
+          const size_t ws = kvattn_mla_workspace_bytes(B, 128, 512, 64, S, bs, split, KVATTN_BF16);
+          CHECK(ws != kRejected && ws > 0, "B=%d S=%d", B, S);
+          if (ws == kRejected) continue;
+          const bool paged = bs > 0;
+          const int32_t maxb = paged ? (S + bs - 1) / bs : 0;
+          const int64_t cache_len = paged ? (int64_t)B * maxb : S;
+          unsigned char* base = reinterpret_cast<unsigned char*>(1 << 20);
+          stub::last = stub::Record{};
+          const kvattn_status st =
+              kvattn_mla_decode(P, P, paged ? PI : nullptr, PI, P, nullptr, B, 128, 512, 64, cache_len, bs, maxb, S,
+                                0.07f, KVATTN_BF16, split, base, ws, nullptr);
+          CHECK(st == KVATTN_OK, "B=%d S=%d split=%d: %s", B, S, split, kvattn_last_error());
+          if (st != KVATTN_OK) continue;
+          CHECK(kvattn_mla_decode(P, P, paged ? PI : nullptr, PI, P, nullptr, B, 128, 512, 64, cache_len, bs, maxb, S,
+                                  0.07f, KVATTN_BF16, split, base, ws - 1, nullptr) == KVATTN_ERR_WORKSPACE,
+                "short MLA workspace");
+          const kvattn::DecodeArgs& a = stub::last.args;
+          // The most pieces the device plan can make: max(256, B) when it chooses (one piece per sequence
+          // always fits), B * ceil(S / split) for a requested length.
+          const int64_t most = split > 0 ? (int64_t)B * ((S + split - 1) / split) : (B > 256 ? B : 256);
+          CHECK(a.max_pieces >= most, "max_pieces %d < %lld", a.max_pieces, (long long)most);
+          auto inside = [&](const void* p, int64_t bytes) {
+            const unsigned char* c = static_cast<const unsigned char*>(p);
+            return c >= base && c + bytes <= base + ws;
+          };
+          CHECK(inside(a.part_o, (int64_t)a.max_pieces * 128 * 512 * 2), "partials outside the workspace");
+          CHECK(inside(a.part_lse, (int64_t)a.max_pieces * 128 * 4), "lse outside");
+          CHECK(inside(a.pieces, (int64_t)a.max_pieces * 16), "pieces outside");
+          CHECK(inside(a.seq_pieces, (int64_t)B * 8), "ranges outside");
+          CHECK(inside(a.plan_count, 8), "count outside");
+          CHECK(stub::last.plan.pieces == a.pieces && stub::last.plan.fixed_chunk == split, "plan args");
+        }
+}
+
+static void fuzz() {
+  // Random (also extreme) arguments: the size queries and the calls must agree, never overflow, and a
+  // call given the queried workspace must not fail for lack of workspace.
+  std::mt19937_64 rng(12345);
+  auto pick = [&](std::initializer_list<int32_t> v) { return *(v.begin() + rng() % v.size()); };
+  for (int i = 0; i < 20000; ++i) {
+    const int32_t B = pick({1, 2, 7, 64, 4096, 65535, 70000, 0, -1});
+    const int32_t g = pick({1, 2, 8, 64, 0});
+    const int32_t h = g * pick({1, 4, 8, 64, 128, 3});
+    const int32_t S = pick({0, 1, 63, 64, 65, 8192, 1 << 20, 1 << 28, (1 << 28) + 1, 2147483647, -5});
+    const int32_t bs = pick({0, 0, 1, 16, 3, 1 << 20});
+    const int32_t W = pick({0, 0, 1, 4096, 2147483647});
+    const int32_t split = pick({0, 0, 64, 4096, 1 << 30, 100});
+    const size_t ws = kvattn_gqa_workspace_bytes(B, h, g, 128, S, bs, split, KVATTN_BF16);
+    if (B < 1 || g < 1 || h < 1 || S < 0 || split % 64 != 0) CHECK(ws == kRejected, "accepted bad sizes");
+    if (ws == kRejected || ws > ((size_t)1 << 50)) continue;
+    if (bs > 0 && (int64_t)((S + bs - 1) / bs) > 2147483647) continue;
+    stub::last = stub::Record{};
+    const kvattn_status st = gqa_window(B, h, g, S, bs, W, split, ws);
+    CHECK(st != KVATTN_ERR_WORKSPACE, "B=%d h=%d g=%d S=%d bs=%d W=%d split=%d: %s", B, h, g, S, bs, W, split,
+          kvattn_last_error());
+    if (st == KVATTN_OK) {
+      const kvattn::DecodeArgs& a = stub::last.args;
+      CHECK(a.split_tokens > 0 && a.n_split >= 1, "split %d n %d", a.split_tokens, a.n_split);
+      CHECK((int64_t)a.split_tokens * a.n_split < ((int64_t)1 << 31), "token arithmetic would overflow int");
+    }
+    const size_t mws = kvattn_mla_workspace_bytes(B, 128, 512, 64, S, bs, split, KVATTN_BF16);
+    if (mws != kRejected && mws < ((size_t)1 << 50)) {
+      const int32_t maxb = bs > 0 ? (S + bs - 1) / bs : 0;
+      const kvattn_status ms = kvattn_mla_decode(P, P, bs > 0 ? PI : nullptr, PI, P, nullptr, B, 128, 512, 64,
+                                                 bs > 0 ? 1 << 20 : (S > 0 ? S : 1), bs, maxb, S, 0.07f, KVATTN_BF16,
+                                                 split, P, mws, nullptr);
+      CHECK(ms != KVATTN_ERR_WORKSPACE, "MLA B=%d S=%d split=%d: %s", B, S, split, kvattn_last_error());
+    }
+  }
+}
+
+int main() {
+  gqa_rejections();
+  window_sweep();
+  mla_sweep();
+  fuzz();
+  std::printf("%d checks, %d failed\n", g_checked, g_failed);
+  return g_failed == 0 ? 0 : 1;
+}

@@ -1,0 +1,15 @@
+// Records of the host-only launcher stand-ins (stub_launch.cpp).
+#pragma once
+
+#include "../../decode_attention_kv_03_amd/csrc/kvattn_internal.h"
+
+namespace stub {
+struct Record {
+  const char* kernel = nullptr;
+  kvattn::DecodeArgs args{};
+  kvattn::MlaPlanArgs plan{};
+  int launches = 0;
+  int merges = 0;
+};
+extern Record last;
+}  // namespace stub

@@ -12,6 +12,7 @@ from decode_attention_kv_03_amd import kvattn as K
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvattn.h")
+MEASURE_HEADER = os.path.join(ROOT, "include", "kvattn_measure.h")
 
 lib = None
 
@@ -23,18 +24,22 @@ def setup_module(_):
     lib = K.load_library()
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kvattn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_functions()
+    measure = header_functions(MEASURE_HEADER)
     assert "kvattn_gqa_decode" in names and "kvattn_mla_decode" in names
-    for n in names:
+    # the attention header holds the operations, sizing queries and error calls only
+    assert not set(names) & set(measure)
+    assert measure == ["kvattn_hbm_read_probe", "kvattn_time_next_kernel"]
+    for n in names + measure:
         assert hasattr(lib, n), n
-    assert sorted(K.SIGNATURES) == names
+    assert sorted(K.SIGNATURES) == sorted(names + measure)
 
 
 def test_status_strings():

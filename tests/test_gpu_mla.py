@@ -143,16 +143,16 @@ def test_rerun_is_bit_identical():
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
-def test_full_size_sampled():
+def test_full_size_every_sequence():
     w = W.WORKLOADS["deepseek_v2_mla_h128_b32_s8192"]
     note(w.name)
     x = W.make_mla_inputs(w, DEV)
     out, lse = run(x)
-    rows = [0, 13, 31]
-    ref, ref_lse = reference(x, rows=rows)
-    assert_close(out[rows].float().cpu().numpy(), ref, w.name)
-    np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
-    assert torch.isfinite(out.float()).all()
+    ref, ref_lse = reference(x)
+    assert_close(out.float().cpu().numpy(), ref, w.name)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    del x
+    torch.cuda.empty_cache()
 
 
 def test_paged_full_size_sampled():
