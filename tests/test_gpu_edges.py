@@ -19,12 +19,14 @@ outside its outputs and workspace.
   oracle.
 
 Tolerances as elsewhere: bf16 and fp8 caches |gpu - ref| <= 2e-2 + 1e-2
-|ref|; fp32 max |gpu - ref| <= 1e-5; lse atol 2e-3 (fp32: 1e-5).
+|ref|; fp32 max |gpu - ref| <= 1e-5; lse atol 4e-3 (fp32: 1e-5), derived in tests/tolerances.py.
 """
 
 import numpy as np
 import pytest
 import torch
+
+from tests.tolerances import LSE_ATOL, LSE_ATOL_F32  # noqa: F401
 
 import oracle
 from decode_attention_kv_03_amd import (gqa_decode, gqa_decode_fp8, gqa_workspace_bytes, mla_decode,
@@ -119,7 +121,7 @@ def test_paged_tiny_blocks_slide_the_staged_table(dtype, block_size, split, lens
     out, lse = gqa_call(x, return_lse=True, split_tokens=split)
     torch.cuda.synchronize()
     assert_close(out.float().cpu().numpy(), ref, f"split={split}")
-    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
     # and with the library's own split (at most 2048 tokens for a paged cache)
     out0 = gqa_call(x, split_tokens=0)
     torch.cuda.synchronize()
@@ -146,7 +148,7 @@ def test_long_single_sequence_gqa(h, g, split, dtype):
     out, lse = gqa_call(x, return_lse=True, split_tokens=split)
     torch.cuda.synchronize()
     assert_close(out.float().cpu().numpy(), ref, "long", f32=dtype == "f32")
-    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=1e-5 if dtype == "f32" else 2e-3, rtol=1e-4)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL_F32 if dtype == "f32" else LSE_ATOL, rtol=1e-4)
 
 
 @pytest.mark.parametrize("h,split", [(128, 0), (16, 64)])
@@ -163,7 +165,7 @@ def test_long_single_sequence_mla(h, split):
     out, lse = mla_decode(x["q"], x["cache"], x["seq_lens"], w.scale, return_lse=True, split_tokens=split)
     torch.cuda.synchronize()
     assert_close(out.float().cpu().numpy(), ref, "long mla")
-    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
 
 
 # ---- many sequences in the MLA plan ----
@@ -185,7 +187,7 @@ def test_mla_600_sequences(split, bs):
     got = lse.cpu().numpy()
     assert np.array_equal(np.isneginf(got), np.isneginf(ref_lse))
     fin = np.isfinite(ref_lse)
-    np.testing.assert_allclose(got[fin], ref_lse[fin], atol=2e-3, rtol=1e-4)
+    np.testing.assert_allclose(got[fin], ref_lse[fin], atol=LSE_ATOL, rtol=1e-4)
 
 
 # ---- guard bands around out, lse and the workspace ----
@@ -223,7 +225,7 @@ def test_gqa_writes_nothing_outside_its_buffers(dtype, B, h, g, lens, bs, split,
     got = lse.tensor.cpu().numpy()
     assert np.array_equal(np.isneginf(got), np.isneginf(ref_lse))
     fin = np.isfinite(ref_lse)
-    np.testing.assert_allclose(got[fin], ref_lse[fin], atol=1e-5 if dtype == "f32" else 2e-3, rtol=1e-4)
+    np.testing.assert_allclose(got[fin], ref_lse[fin], atol=LSE_ATOL_F32 if dtype == "f32" else LSE_ATOL, rtol=1e-4)
 
 
 @pytest.mark.parametrize("B,h,lens,bs,split", [(3, 128, [2000, 31, 700], 0, 0), (4, 64, [900, 0, 65, 500], 16, 64),
@@ -247,7 +249,7 @@ def test_mla_writes_nothing_outside_its_buffers(B, h, lens, bs, split):
     got = lse.tensor.cpu().numpy()
     assert np.array_equal(np.isneginf(got), np.isneginf(ref_lse))
     fin = np.isfinite(ref_lse)
-    np.testing.assert_allclose(got[fin], ref_lse[fin], atol=2e-3, rtol=1e-4)
+    np.testing.assert_allclose(got[fin], ref_lse[fin], atol=LSE_ATOL, rtol=1e-4)
 
 
 # ---- out-of-range block-table entries ----

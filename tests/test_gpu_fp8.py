@@ -4,12 +4,14 @@ Tolerance: |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise, as for a bf16 cache:
 every E4M3 value widens exactly to bf16, so the kernel's only roundings are
 those of the bf16 path (probabilities fed to the matrix cores as bf16, fp32
 accumulation, bf16 output) plus the fp32 product of the softmax scale and
-the K scale.  Log-sum-exp: atol 2e-3, rtol 1e-4.
+the K scale.  Log-sum-exp: atol 4e-3 (derived in tests/tolerances.py), rtol 1e-4.
 """
 
 import numpy as np
 import pytest
 import torch
+
+from tests.tolerances import LSE_ATOL, LSE_ATOL_F32  # noqa: F401
 
 import oracle
 from decode_attention_kv_03_amd import gqa_decode_fp8
@@ -88,7 +90,7 @@ def test_fp8_contiguous_ragged_with_poisoned_tail(B, h, g, lens, split):
     ref, ref_lse = reference(x)
     out, lse = run(x, split_tokens=split)
     assert_close(out.float().cpu().numpy(), ref)
-    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
 
 
 @pytest.mark.parametrize("B,h,g,lens,window,split", [
@@ -104,7 +106,7 @@ def test_fp8_sliding_window(B, h, g, lens, window, split):
     ref, ref_lse = reference(x, window=window)
     out, lse = run(x, split_tokens=split, window=window)
     assert_close(out.float().cpu().numpy(), ref, f"window={window}")
-    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
 
 
 @pytest.mark.parametrize("B,h,g,max_len,block_size,window", [
@@ -124,7 +126,7 @@ def test_fp8_paged(B, h, g, max_len, block_size, window):
     for split in (0, 64, 256):
         out, lse = run(x, split_tokens=split, window=window)
         assert_close(out.float().cpu().numpy(), ref, f"split={split}")
-        np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+        np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
 
 
 def test_fp8_zero_lengths_and_scales():
@@ -145,7 +147,7 @@ def test_fp8_zero_lengths_and_scales():
     ref2, ref2_lse = reference(x2)
     out2, lse2 = run(x2)
     assert_close(out2.float().cpu().numpy(), ref2, "rescaled")
-    np.testing.assert_allclose(lse2.cpu().numpy(), ref2_lse, atol=2e-3, rtol=1e-4)
+    np.testing.assert_allclose(lse2.cpu().numpy(), ref2_lse, atol=LSE_ATOL, rtol=1e-4)
 
 
 def test_fp8_rerun_is_bit_identical():
@@ -166,7 +168,7 @@ def test_fp8_full_size_sampled():
     rows = [0, 31, 63]
     ref, ref_lse = reference(x, rows=rows)
     assert_close(out[rows].float().cpu().numpy(), ref, w.name)
-    np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-4)
+    np.testing.assert_allclose(lse[rows].cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
     assert torch.isfinite(out.float()).all()
     del x
     torch.cuda.empty_cache()
