@@ -23,6 +23,7 @@ from .kvattn import (  # noqa: F401
     KvattnError,
     gqa_decode,
     gqa_decode_fp8,
+    gqa_decode_noalloc,
     gqa_workspace_bytes,
     hbm_read_probe,
     library_path,

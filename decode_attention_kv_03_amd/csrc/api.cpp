@@ -116,9 +116,10 @@ int32_t n_splits(int32_t max_seq_len, int32_t split) {
   return (int32_t)(((int64_t)max_seq_len + split - 1) / split);
 }
 
-size_t partial_bytes(int64_t batch, int64_t heads, int64_t nsplit, int64_t d_v) {
+// Split-K partials: outputs of `part_elem` bytes per element, then one fp32 log-sum-exp per row.
+size_t partial_bytes(int64_t batch, int64_t heads, int64_t nsplit, int64_t d_v, int64_t part_elem = 4) {
   if (nsplit <= 1) return 0;
-  return (size_t)(batch * heads * nsplit * (d_v + 1) * (int64_t)sizeof(float));
+  return (size_t)(batch * heads * nsplit * (d_v * part_elem + (int64_t)sizeof(float)));
 }
 
 kvattn_status check_split(int32_t split_tokens) {
@@ -215,7 +216,7 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
                       const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse, int32_t batch,
                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t cache_len,
                       int32_t block_size, int32_t max_blocks_per_seq, int32_t max_seq_len, float scale,
-                      int32_t window, int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+                      int32_t window, int32_t split_tokens, const kvattn::Workspace& wsrc, void* stream) {
   kvattn_status st;
   if (window < 0) return fail(KVATTN_ERR_INVALID, "window must be >= 0 (0: attend to all tokens), got %lld", window);
   const bool paged = block_table != nullptr;
@@ -241,10 +242,23 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
       nsplit = n_splits(span, split);
     }
   }
-  const size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-    return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
-                workspace == nullptr ? 0 : (long long)workspace_bytes);
+  // Partial outputs are fp32 for an fp32 cache and bf16 otherwise (the
+  // workspace query sizes the fp32 layout, which bounds both).
+  const size_t part_elem = cache.kind == CacheKind::kF32 ? sizeof(float) : sizeof(uint16_t);
+  const size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim, (int64_t)part_elem);
+  void* workspace = wsrc.ptr;
+  if (need > 0) {
+    if (wsrc.resolve != nullptr) {
+      // The library's own scratch: its size is checked before it is looked up.
+      if (need > wsrc.bytes)
+        return fail(KVATTN_ERR_WORKSPACE, "this call needs %lld bytes of scratch; the no-allocation entry point "
+                    "holds %lld (use the entry point that takes a workspace)", (long long)need, (long long)wsrc.bytes);
+      if ((st = wsrc.resolve(&workspace)) != KVATTN_OK) return st;
+    } else if (workspace == nullptr || wsrc.bytes < need) {
+      return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)need,
+                  workspace == nullptr ? 0 : (long long)wsrc.bytes);
+    }
+  }
 
   kvattn::DecodeArgs a{};
   a.q = q;
@@ -270,10 +284,8 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   a.n_split = nsplit;
   a.scale_log2 = scale * kvattn::kLog2eHost;
   if (nsplit > 1) {
-    // Partial outputs (fp32 for an fp32 cache, bf16 otherwise), then the
-    // fp32 log-sum-exps; partial_bytes sizes the fp32 layout, which bounds both.
+    // Partial outputs, then the fp32 log-sum-exps.
     const int64_t n_part = (int64_t)batch * num_q_heads * nsplit * head_dim;
-    const size_t part_elem = cache.kind == CacheKind::kF32 ? sizeof(float) : sizeof(uint16_t);
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + n_part * part_elem);
   }
@@ -293,6 +305,28 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
 }
 
 }  // namespace
+
+namespace kvattn {
+
+kvattn_status gqa_decode_with(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, void* out, float* lse, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int64_t cache_len, int32_t block_size,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len, float scale, int32_t window,
+                              kvattn_dtype dtype, int32_t split_tokens, const Workspace& ws, void* stream) {
+  const LaunchEvents ev = take_timing_events();  // armed for this call only, whatever its outcome
+  kvattn_status st = check_gqa(q, k_cache, v_cache, seq_lens, out, batch, num_q_heads, num_kv_heads, head_dim, dtype,
+                               scale);
+  if (st != KVATTN_OK) return st;
+  const GqaCache cache{k_cache, v_cache, nullptr, nullptr, dtype == KVATTN_BF16 ? CacheKind::kBf16 : CacheKind::kF32};
+  return gqa_run(ev, q, cache, block_table, seq_lens, out, lse, batch, num_q_heads, num_kv_heads, head_dim,
+                 cache_len, block_size, max_blocks_per_seq, max_seq_len, scale, window, split_tokens, ws, stream);
+}
+
+kvattn_status report(kvattn_status s, const char* what, long long a, long long b) { return fail(s, what, a, b); }
+
+kvattn_status report_hip(hipError_t e, const char* what) { return hip_status(e, what); }
+
+}  // namespace kvattn
 
 extern "C" {
 
@@ -361,14 +395,10 @@ kvattn_status kvattn_gqa_decode_window(const void* q, const void* k_cache, const
                                        int64_t cache_len, int32_t block_size, int32_t max_blocks_per_seq,
                                        int32_t max_seq_len, float scale, int32_t window, kvattn_dtype dtype,
                                        int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
-  const kvattn::LaunchEvents ev = take_timing_events();  // armed for this call only, whatever its outcome
-  kvattn_status st = check_gqa(q, k_cache, v_cache, seq_lens, out, batch, num_q_heads, num_kv_heads, head_dim, dtype,
-                               scale);
-  if (st != KVATTN_OK) return st;
-  const GqaCache cache{k_cache, v_cache, nullptr, nullptr, dtype == KVATTN_BF16 ? CacheKind::kBf16 : CacheKind::kF32};
-  return gqa_run(ev, q, cache, block_table, seq_lens, out, lse, batch, num_q_heads, num_kv_heads, head_dim,
-                 cache_len, block_size, max_blocks_per_seq, max_seq_len, scale, window, split_tokens, workspace,
-                 workspace_bytes, stream);
+  return kvattn::gqa_decode_with(q, k_cache, v_cache, block_table, seq_lens, out, lse, batch, num_q_heads,
+                                 num_kv_heads, head_dim, cache_len, block_size, max_blocks_per_seq, max_seq_len, scale,
+                                 window, dtype, split_tokens, kvattn::Workspace{workspace, workspace_bytes, nullptr},
+                                 stream);
 }
 
 kvattn_status kvattn_gqa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
@@ -385,8 +415,8 @@ kvattn_status kvattn_gqa_decode_fp8(const void* q, const void* k_cache, const vo
   if (!k_scale || !v_scale) return fail(KVATTN_ERR_INVALID, "k_scale and v_scale must be non-null");
   const GqaCache cache{k_cache, v_cache, k_scale, v_scale, CacheKind::kFp8E4m3};
   return gqa_run(ev, q, cache, block_table, seq_lens, out, lse, batch, num_q_heads, num_kv_heads, head_dim,
-                 cache_len, block_size, max_blocks_per_seq, max_seq_len, scale, window, split_tokens, workspace,
-                 workspace_bytes, stream);
+                 cache_len, block_size, max_blocks_per_seq, max_seq_len, scale, window, split_tokens,
+                 kvattn::Workspace{workspace, workspace_bytes, nullptr}, stream);
 }
 
 kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t* block_table, const int32_t* seq_lens,

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/kvattn.h"
+
 namespace kvattn {
 
 constexpr int kHeadDim = 128;      // GQA head width the kernels are built for
@@ -75,6 +77,25 @@ struct LaunchEvents {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
+
+// Where a call's split-K workspace comes from: the caller's buffer (ptr,
+// bytes), or, when `resolve` is set, the library's fixed scratch of `bytes`
+// bytes, looked up through `resolve` only after the call's size checks pass.
+struct Workspace {
+  void* ptr;
+  size_t bytes;
+  kvattn_status (*resolve)(void** ptr);
+};
+
+// kvattn_gqa_decode_window with its workspace taken from `ws` (api.cpp).
+kvattn_status gqa_decode_with(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, void* out, float* lse, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int64_t cache_len, int32_t block_size,
+                              int32_t max_blocks_per_seq, int32_t max_seq_len, float scale, int32_t window,
+                              kvattn_dtype dtype, int32_t split_tokens, const Workspace& ws, void* stream);
+// Record a failure (printf-style detail with up to two integers) / a HIP error as the thread's last error.
+kvattn_status report(kvattn_status s, const char* what, long long a = 0, long long b = 0);
+kvattn_status report_hip(hipError_t e, const char* what);
 
 hipError_t launch_gqa_f32(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);

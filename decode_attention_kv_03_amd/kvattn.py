@@ -32,6 +32,11 @@ SIGNATURES = {
         [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
          _c_i32, _c_f32, _c_i32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
     ),
+    "kvattn_gqa_decode_noalloc": (
+        _c_i32,
+        [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32,
+         _c_i32, _c_f32, _c_i32, _c_i32, _c_i32, _c_vp],
+    ),
     "kvattn_gqa_decode_fp8": (
         _c_i32,
         [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
@@ -239,6 +244,40 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale, *, block_table=None, max_se
             B, h, g, d, cache_len, block_size, max_blocks, max_seq_len, float(scale), code, int(split_tokens),
             _ptr(ws), nbytes, _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def gqa_decode_noalloc(q, k_cache, v_cache, seq_lens, scale, out, *, block_table=None, max_seq_len=None, lse=None,
+                       split_tokens=0, stream=None, window=0):
+    """``gqa_decode`` through kvattn_gqa_decode_noalloc: no workspace, nothing allocated.
+
+    The caller passes the output (and optionally lse) tensors; the split-K
+    partials go to the library's fixed per-GPU scratch array
+    (``NOALLOC_SCRATCH_BYTES``).  Calls that could overlap on one GPU race on
+    that array.  Returns ``out`` (and ``lse`` when given).
+    """
+    _need_gpu(q, k_cache, v_cache, seq_lens, block_table, out, lse)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("kvattn: q must be [B, h, d] and the caches 4-d with equal shapes")
+    code = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("kvattn: q, k_cache and v_cache must share a dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],):
+        raise ValueError("kvattn: seq_lens must be int32 [B]")
+    B, h, d = q.shape
+    g, cache_len, block_size, max_blocks, max_seq_len = _gqa_geometry(q, k_cache, block_table, max_seq_len)
+    if out.shape != (B, h, d) or out.dtype != q.dtype:
+        raise ValueError("kvattn: out must be [B, h, d] with the dtype of q")
+    if lse is not None and (lse.shape != (B, h) or lse.dtype != torch.float32):
+        raise ValueError("kvattn: lse must be float32 [B, h]")
+    lib = load_library()
+    _check(lib.kvattn_gqa_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), B, h, g, d,
+        cache_len, block_size, max_blocks, max_seq_len, float(scale), int(window), code, int(split_tokens),
+        _stream(stream)))
+    return (out, lse) if lse is not None else out
 
 
 def gqa_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, scale, *, block_table=None, max_seq_len=None,

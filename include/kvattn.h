@@ -152,6 +152,37 @@ kvattn_status kvattn_gqa_decode_window(const void* q, const void* k_cache, const
                                        size_t workspace_bytes, void* stream);
 
 /*
+ * kvattn_gqa_decode_window without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The split-K partials go to a
+ * scratch array of KVATTN_NOALLOC_SCRATCH_BYTES bytes that the library keeps
+ * in device memory, one per GPU it runs on, from the first call on that GPU
+ * until the process ends.  The call allocates, frees and clears nothing
+ * (the partials need no initialisation); the first call on a device looks up
+ * the array's address there, a host-side query.
+ *
+ * Arguments, layouts, results and errors are those of
+ * kvattn_gqa_decode_window (window 0: every token), with the same split
+ * planning, so the results equal that call's bit for bit.  A call whose
+ * partials need more than KVATTN_NOALLOC_SCRATCH_BYTES (bf16: batch *
+ * num_q_heads * splits * (2 * head_dim + 4) bytes when it splits; fp32: 4 *
+ * head_dim + 4 per row and split) returns KVATTN_ERR_WORKSPACE before any HIP
+ * call; kvattn_gqa_split_tokens gives the split size it would use.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (on different streams, or from different threads without ordering)
+ * race on it and must not be issued together.
+ */
+#define KVATTN_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+kvattn_status kvattn_gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                                        int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int64_t cache_len, int32_t block_size, int32_t max_blocks_per_seq,
+                                        int32_t max_seq_len, float scale, int32_t window, kvattn_dtype dtype,
+                                        int32_t split_tokens, void* stream);
+
+/*
  * Grouped-query decode over an FP8 KV cache.  Storing the cache in fp8 halves
  * its bytes, and a GQA cache quantises at the granularity of one KV head
  * ("Why GQA's KV Cache Savings Don't Fully Reduce TPOT", section "When the

@@ -79,7 +79,11 @@ static void gqa_rejections() {
   CHECK(gqa_window(2, 128, 1, 64, 0, 0, 0, 0, KVATTN_F32) == KVATTN_ERR_UNSUPPORTED, "fp32 group 128");
   const size_t need = kvattn_gqa_workspace_bytes(2, 8, 2, 128, 4096, 0, 256, KVATTN_BF16);
   CHECK(need == (size_t)2 * 8 * 16 * 129 * 4, "need %zu", need);
-  CHECK(gqa_window(2, 8, 2, 4096, 0, 0, 256, need - 1) == KVATTN_ERR_WORKSPACE, "short workspace");
+  // the call itself needs the bf16 layout: bf16 partial outputs and fp32 log-sum-exps
+  const size_t need_bf16 = (size_t)2 * 8 * 16 * (128 * 2 + 4);
+  CHECK(gqa_window(2, 8, 2, 4096, 0, 0, 256, need_bf16 - 1) == KVATTN_ERR_WORKSPACE, "short workspace");
+  CHECK(gqa_window(2, 8, 2, 4096, 0, 0, 256, need_bf16) == KVATTN_OK, "%s", kvattn_last_error());
+  CHECK(gqa_window(2, 8, 2, 4096, 0, 0, 256, need - 1, KVATTN_F32) == KVATTN_ERR_WORKSPACE, "short fp32 workspace");
   CHECK(gqa_window(2, 8, 2, 4096, 0, 0, 256, need) == KVATTN_OK, "%s", kvattn_last_error());
 }
 
@@ -163,7 +167,49 @@ static void fuzz() {
   }
 }
 
+// The no-allocation path (kvattn_gqa_decode_noalloc) takes its workspace from a fixed scratch: the size
+// check comes first, and the scratch is looked up only by a call that needs it and fits.
+static int g_resolved = 0;
+static kvattn_status fake_scratch(void** p) {
+  ++g_resolved;
+  *p = reinterpret_cast<void*>(1 << 24);
+  return KVATTN_OK;
+}
+
+static void scratch_source() {
+  const size_t cap = KVATTN_NOALLOC_SCRATCH_BYTES;
+  struct Case {
+    int32_t B, h, g, S, bs, split;
+    kvattn_dtype dt;
+  } cases[] = {{2, 8, 2, 64, 0, 0, KVATTN_BF16},          {16, 32, 8, 8192, 0, 0, KVATTN_BF16},
+               {128, 64, 8, 32768, 16, 0, KVATTN_BF16},   {128, 64, 8, 32768, 16, 0, KVATTN_F32},
+               {512, 64, 8, 32768, 16, 0, KVATTN_BF16},   {1, 128, 1, 65536, 0, 64, KVATTN_BF16},
+               {64, 64, 1, 8192, 0, 64, KVATTN_F32}};
+  for (const Case& c : cases) {
+    const int32_t maxb = c.bs ? (c.S + c.bs - 1) / c.bs : 0;
+    const int64_t cache_len = c.bs ? (int64_t)c.B * maxb : c.S;
+    g_resolved = 0;
+    stub::last = stub::Record{};
+    const kvattn_status st = kvattn::gqa_decode_with(
+        P, P, P, c.bs ? PI : nullptr, PI, P, nullptr, c.B, c.h, c.g, 128, cache_len, c.bs, maxb, c.S, 0.1f, 0, c.dt,
+        c.split, kvattn::Workspace{nullptr, cap, fake_scratch}, nullptr);
+    const int32_t split = kvattn_gqa_split_tokens(c.B, c.h, c.g, c.S, c.bs, c.split);
+    const int64_t nsplit = c.S <= split ? 1 : (c.S + split - 1) / split;
+    const int64_t elem = c.dt == KVATTN_F32 ? 4 : 2;
+    const int64_t need = nsplit > 1 ? (int64_t)c.B * c.h * nsplit * (128 * elem + 4) : 0;
+    if (need > (int64_t)cap) {
+      CHECK(st == KVATTN_ERR_WORKSPACE && g_resolved == 0 && stub::last.launches == 0, "B=%d need %lld: st %d",
+            c.B, (long long)need, st);
+    } else {
+      CHECK(st == KVATTN_OK, "B=%d S=%d: %s", c.B, c.S, kvattn_last_error());
+      CHECK(g_resolved == (need > 0 ? 1 : 0), "looked up %d times", g_resolved);
+      if (need > 0) CHECK(stub::last.args.part_o == reinterpret_cast<float*>(1 << 24), "partials not in the scratch");
+    }
+  }
+}
+
 int main() {
+  scratch_source();
   gqa_rejections();
   window_sweep();
   mla_sweep();

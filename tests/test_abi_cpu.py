@@ -107,7 +107,11 @@ def test_gqa_workspace_required_when_split():
     need = lib.kvattn_gqa_workspace_bytes(2, 8, 2, 128, 4096, 0, 256, K.KVATTN_BF16)
     assert need == 2 * 8 * 16 * 129 * 4  # 16 splits of partial outputs and log-sum-exps
     assert gqa(cache_len=4096, maxlen=4096, split=256, ws=None, wsb=0) == K.KVATTN_ERR_WORKSPACE
-    assert gqa(cache_len=4096, maxlen=4096, split=256, ws=P, wsb=need - 1) == K.KVATTN_ERR_WORKSPACE
+    # the call needs the bytes of its own layout: bf16 partial outputs (fp32 ones for an fp32 call)
+    need_bf16 = 2 * 8 * 16 * (128 * 2 + 4)
+    assert gqa(cache_len=4096, maxlen=4096, split=256, ws=P, wsb=need_bf16 - 1) == K.KVATTN_ERR_WORKSPACE
+    assert gqa(cache_len=4096, maxlen=4096, split=256, ws=P, wsb=need - 1, dtype=K.KVATTN_F32) == \
+        K.KVATTN_ERR_WORKSPACE
     # a single split needs none
     assert lib.kvattn_gqa_workspace_bytes(2, 8, 2, 128, 256, 0, 256, K.KVATTN_BF16) == 0
     assert lib.kvattn_gqa_workspace_bytes(2, 8, 3, 128, 256, 0, 0, K.KVATTN_BF16) == ctypes.c_size_t(-1).value
@@ -197,4 +201,20 @@ def test_time_next_kernel_arms_both_events_or_none():
     assert lib.kvattn_time_next_kernel(fake, fake) == K.KVATTN_OK
     st = lib.kvattn_gqa_decode(None, None, None, None, None, None, None, 1, 8, 2, 128, 16, 0, 0, 16, 0.1,
                                K.KVATTN_BF16, 0, None, 0, None)
+    assert st == K.KVATTN_ERR_INVALID
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_before_touching_the_gpu():
+    """A call whose partials exceed the fixed scratch fails on the host, with a message that says so."""
+    cap = K.NOALLOC_SCRATCH_BYTES
+    # 4 sequences x 128 heads x 1024 splits of 64 tokens x (2 x 128 + 4) bytes = 136 MB > 128 MiB
+    B, h, g, S = 4, 128, 1, 65536
+    assert B * h * (S // 64) * (2 * 128 + 4) > cap
+    st = lib.kvattn_gqa_decode_noalloc(P, P, P, None, P, P, None, B, h, g, 128, S, 0, 0, S, 0.1, 0, K.KVATTN_BF16, 64,
+                                       None)
+    assert st == K.KVATTN_ERR_WORKSPACE
+    assert b"no-allocation" in lib.kvattn_last_error()
+    # argument errors come first, as for the other entry points
+    st = lib.kvattn_gqa_decode_noalloc(P, P, P, None, P, P, None, B, h, 3, 128, S, 0, 0, S, 0.1, 0, K.KVATTN_BF16, 64,
+                                       None)
     assert st == K.KVATTN_ERR_INVALID
