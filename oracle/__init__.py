@@ -35,6 +35,8 @@ from .attention import (  # noqa: F401
     paged_mla_absorbed_decode,
     mla_absorb_query,
     mla_explicit_decode,
+    mla_explicit_decode_batch,
+    mla_up_project,
     lse_merge,
 )
 from .fp8 import (  # noqa: F401

@@ -220,6 +220,46 @@ def mla_explicit_decode(q_c, q_r, c, k_r, W_uk, W_uv, scale):
     return np.stack(outs), np.array(lses)
 
 
+def mla_up_project(o_latent, W_uv):
+    """Move absorbed MLA outputs from latent space to each head's value space.
+
+    o_latent: [..., h, d_c] (the absorbed form's ``sum_t p_t c_t`` per head);
+    W_uv: [h, d_c, d_v].  Since ``v_i = c W_uv^(i)`` (section 5 of "MQA, GQA,
+    and MLA") and the attention average is linear, head ``i``'s output is
+    ``o_latent_i W_uv^(i)``.  Returns [..., h, d_v].
+    """
+    o_latent = np.asarray(o_latent, dtype=np.float64)
+    W_uv = np.asarray(W_uv, dtype=np.float64)
+    h = o_latent.shape[-2]
+    out = np.empty(o_latent.shape[:-1] + (W_uv.shape[2],), dtype=np.float64)
+    for i in range(h):
+        out[..., i, :] = o_latent[..., i, :] @ W_uv[i]
+    return out
+
+
+def mla_explicit_decode_batch(q, cache, seq_lens, W_uk, W_uv, scale, d_c=512, bf16=False):
+    """``mla_explicit_decode`` for a batch over a contiguous latent cache.
+
+    q: [B, h, d_h + d_r] rows ``[q^C_i | q^R_i]``; cache: [B, S, d_c + d_r]
+    rows ``[c_t | k^R_t]``; W_uk: [h, d_c, d_h]; W_uv: [h, d_c, d_v].
+    Sequence ``b`` attends over its first ``seq_lens[b]`` rows.  With
+    ``bf16=True`` every array holds bfloat16 bit patterns.  Returns
+    (o [B, h, d_v], lse [B, h]).
+    """
+    W_uk = _f64(W_uk, bf16)
+    W_uv = _f64(W_uv, bf16)
+    d_h = W_uk.shape[2]
+    B, h, _ = q.shape
+    o = np.zeros((B, h, W_uv.shape[2]), dtype=np.float64)
+    lse = np.full((B, h), -np.inf, dtype=np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        qb = _f64(q[b], bf16)
+        rows = _f64(cache[b, :n], bf16)
+        o[b], lse[b] = mla_explicit_decode(qb[:, :d_h], qb[:, d_h:], rows[:, :d_c], rows[:, d_c:], W_uk, W_uv, scale)
+    return o, lse
+
+
 def lse_merge(parts):
     """Combine attention results computed over disjoint token subsets.
 

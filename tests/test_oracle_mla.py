@@ -40,10 +40,55 @@ def test_absorbed_equals_explicit_reconstruction(h, d_c, d_r, d_h, d_v, n):
     q_abs = np.concatenate([oracle.mla_absorb_query(q_c, W_uk), q_r], axis=1)[None]
     cache = np.concatenate([c, k_r], axis=1)[None]
     o_lat, lse_abs = oracle.mla_absorbed_decode(q_abs, cache, [n], scale, d_c=d_c)
-    o_abs = np.stack([o_lat[0, i] @ W_uv[i] for i in range(h)])
+    o_abs = oracle.mla_up_project(o_lat, W_uv)[0]
 
     np.testing.assert_allclose(o_abs, o_exp, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse_abs[0], lse_exp, rtol=0, atol=1e-12)
+
+
+def test_batched_explicit_equals_absorbed_then_up_projected():
+    """Exercise D over a batch of ragged sequences (one empty), in the layouts the library takes:
+    q rows [q^C | q^R], cache rows [c | k^R], W_uk [h, d_c, d_h], W_uv [h, d_c, d_v]."""
+    rng = np.random.default_rng(11)
+    B, h, d_c, d_r, d_h, d_v, S = 3, 4, 16, 4, 8, 6, 9
+    W_uk, W_uv = _weights(rng, h, d_c, d_h, d_v)
+    q = rng.standard_normal((B, h, d_h + d_r))
+    cache = rng.standard_normal((B, S, d_c + d_r))
+    lens = [9, 0, 4]
+    scale = 1 / math.sqrt(d_h + d_r)
+    o_exp, lse_exp = oracle.mla_explicit_decode_batch(q, cache, lens, W_uk, W_uv, scale, d_c=d_c)
+    q_abs = np.concatenate([np.stack([oracle.mla_absorb_query(q[b, :, :d_h], W_uk) for b in range(B)]),
+                            q[..., d_h:]], axis=2)
+    o_lat, lse_abs = oracle.mla_absorbed_decode(q_abs, cache, lens, scale, d_c=d_c)
+    np.testing.assert_allclose(oracle.mla_up_project(o_lat, W_uv), o_exp, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(lse_exp), np.isneginf(lse_abs))
+    fin = np.isfinite(lse_exp)
+    np.testing.assert_allclose(lse_abs[fin], lse_exp[fin], rtol=0, atol=1e-12)
+    assert np.all(o_exp[1] == 0) and np.all(np.isneginf(lse_exp[1]))
+    # each sequence alone gives the same rows
+    for b in range(B):
+        o1, _ = oracle.mla_explicit_decode(q[b, :, :d_h], q[b, :, d_h:], cache[b, :lens[b], :d_c],
+                                           cache[b, :lens[b], d_c:], W_uk, W_uv, scale)
+        np.testing.assert_array_equal(o1, o_exp[b])
+
+
+def test_up_projection_closed_forms():
+    rng = np.random.default_rng(12)
+    h, d_c = 3, 8
+    o_lat = rng.standard_normal((2, h, d_c))
+    # identity weights return the latent output itself
+    eye = np.stack([np.eye(d_c)] * h)
+    np.testing.assert_array_equal(oracle.mla_up_project(o_lat, eye), o_lat)
+    # a weight that selects latent column j for value column k: out[..., i, k] = o_lat[..., i, j]
+    W = np.zeros((h, d_c, 2))
+    W[0, 5, 0] = 1.0
+    W[1, 2, 1] = 1.0
+    W[2, 7, 0] = 3.0
+    out = oracle.mla_up_project(o_lat, W)
+    np.testing.assert_array_equal(out[:, 0, 0], o_lat[:, 0, 5])
+    np.testing.assert_array_equal(out[:, 1, 1], o_lat[:, 1, 2])
+    np.testing.assert_array_equal(out[:, 2, 0], 3.0 * o_lat[:, 2, 7])
+    assert np.all(out[:, 0, 1] == 0) and np.all(out[:, 1, 0] == 0)
 
 
 def test_absorbed_query_scores_equal_reconstructed_key_scores():

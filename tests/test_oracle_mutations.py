@@ -173,3 +173,36 @@ def test_formula_mistakes_are_caught(monkeypatch, name, mutant):
         _fails(TF.test_printed_cache_bytes, row) for row in read_tsv("cache_bytes_printed.tsv") if row[1] == name
     ]
     assert any(failed)
+
+
+def up_project_transposed(o_latent, W_uv):
+    # plausible mistake: each head's weight read as [d_v, d_c] (reshaped, not transposed, when d_v != d_c)
+    o_latent = np.asarray(o_latent, dtype=np.float64)
+    h, d_c, d_v = W_uv.shape
+    return np.stack([o_latent[..., i, :] @ np.asarray(W_uv[i]).reshape(d_v, d_c).T.reshape(d_c, d_v)
+                     for i in range(h)], axis=-2)
+
+
+def up_project_wrong_head(o_latent, W_uv):
+    # plausible mistake: every head projected with head 0's weights
+    o_latent = np.asarray(o_latent, dtype=np.float64)
+    return np.stack([o_latent[..., i, :] @ W_uv[0] for i in range(o_latent.shape[-2])], axis=-2)
+
+
+def test_up_projection_mistakes_are_caught(monkeypatch):
+    _patch(monkeypatch, "mla_up_project", up_project_wrong_head)
+    assert _fails(TM.test_absorbed_equals_explicit_reconstruction, 4, 16, 4, 8, 8, 7)
+    assert _fails(TM.test_batched_explicit_equals_absorbed_then_up_projected)
+    assert _fails(TM.test_up_projection_closed_forms)
+    _patch(monkeypatch, "mla_up_project", up_project_transposed)
+    assert _fails(TM.test_up_projection_closed_forms)
+
+
+def test_explicit_batch_mistakes_are_caught(monkeypatch):
+    orig = A.mla_explicit_decode_batch
+
+    def values_from_keys(q, cache, seq_lens, W_uk, W_uv, scale, d_c=512, bf16=False):
+        return orig(q, cache, seq_lens, W_uk, W_uk[:, :, :W_uv.shape[2]], scale, d_c=d_c, bf16=bf16)
+
+    _patch(monkeypatch, "mla_explicit_decode_batch", values_from_keys)
+    assert _fails(TM.test_batched_explicit_equals_absorbed_then_up_projected)
