@@ -12,6 +12,10 @@ Two operations, both hand-written HIP kernels behind a C ABI
 * ``mla_decode`` -- absorbed multi-head latent attention decode: every head
   scores an absorbed 576-wide query against cached ``[latent 512 | RoPE 64]``
   rows and accumulates its output in the 512-wide latent space.
+* ``mla_up_project`` / ``mla_absorb_query`` (``mla_project``) -- the per-head
+  projections out of and into the latent space on the matrix cores.
+* ``mla_explicit_decode`` -- the naive reconstruct-then-attend MLA decode,
+  which rebuilds per-head keys and values from the latent cache.
 
 The Python layer only marshals arguments (device pointers, sizes, the
 current HIP stream); every arithmetic step runs in the library's kernels.
@@ -28,7 +32,12 @@ from .kvattn import (  # noqa: F401
     hbm_read_probe,
     library_path,
     load_library,
+    mla_absorb_query,
     mla_decode,
+    mla_explicit_decode,
+    mla_explicit_workspace_bytes,
+    mla_project,
+    mla_up_project,
     mla_workspace_bytes,
     time_next_kernel,
 )

@@ -304,6 +304,80 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   return ok();
 }
 
+// Reconstruct-then-attend MLA: per-head K and V rows rebuilt from the latent
+// cache ([B, h, max_seq_len, 128] bf16 each), then the split partials (bf16
+// outputs, fp32 log-sum-exps), each region 256-byte aligned.  Sizes in
+// 128-bit arithmetic; total 0 when they overflow (the caller rejects it).
+struct ExplicitWorkspace {
+  size_t kc, v, part_o, part_lse, total;
+};
+constexpr int32_t kExplicitHead = 128;  // reconstructed content-key and value width
+ExplicitWorkspace explicit_workspace(int64_t batch, int64_t heads, int64_t max_seq_len, int64_t nsplit) {
+  typedef unsigned __int128 u128;
+  auto up = [](u128 x) { return (x + 255) / 256 * 256; };
+  const u128 rows = (u128)batch * heads * (u128)max_seq_len;
+  const u128 rec = up(rows * kExplicitHead * 2);
+  const u128 po = nsplit > 1 ? up((u128)batch * heads * nsplit * kExplicitHead * 2) : 0;
+  const u128 pl = nsplit > 1 ? up((u128)batch * heads * nsplit * 4) : 0;
+  const u128 total = 2 * rec + po + pl;
+  ExplicitWorkspace w{};
+  if (total >= ((u128)1 << 56)) return w;
+  w.kc = 0;
+  w.v = (size_t)rec;
+  w.part_o = (size_t)(2 * rec);
+  w.part_lse = (size_t)(2 * rec + po);
+  w.total = (size_t)total;
+  return w;
+}
+
+kvattn_status check_project(const void* x, const void* w, const void* y, int32_t outer, int32_t heads, int32_t rows,
+                            int32_t k_dim, int32_t n_dim, int64_t xo, int64_t xh, int64_t xr, int64_t wh, int64_t yo,
+                            int64_t yh, int64_t yr, kvattn_dtype dtype) {
+  if (!x || !w || !y) return fail(KVATTN_ERR_INVALID, "x, w and y must be non-null");
+  if (outer < 1 || heads < 1 || rows < 0)
+    return fail(KVATTN_ERR_INVALID, "outer and heads must be >= 1 and rows >= 0 (outer=%lld, heads=%lld)", outer, heads);
+  if (k_dim < 1 || n_dim < 1) return fail(KVATTN_ERR_INVALID, "k_dim and n_dim must be >= 1 (%lld, %lld)", k_dim, n_dim);
+  if (dtype != KVATTN_F32 && dtype != KVATTN_BF16) return fail(KVATTN_ERR_INVALID, "unknown dtype %lld", (int)dtype);
+  if (dtype != KVATTN_BF16) return fail(KVATTN_ERR_UNSUPPORTED, "projections are bf16 only");
+  if (k_dim % 64 != 0 || n_dim % 128 != 0)
+    return fail(KVATTN_ERR_UNSUPPORTED, "k_dim must be a multiple of 64 and n_dim of 128 (%lld, %lld)", k_dim, n_dim);
+  const int64_t strides[] = {xo, xh, xr, wh, yo, yh, yr};
+  for (int64_t st : strides)
+    if (st < 0 || st % 8 != 0) return fail(KVATTN_ERR_INVALID, "strides must be non-negative multiples of 8 elements (got %lld)", st);
+  if (xr < k_dim || yr < n_dim)
+    return fail(KVATTN_ERR_INVALID, "row strides must cover a row (x_row_stride %lld, y_row_stride %lld)", xr, yr);
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(y)) % 16 != 0)
+    return fail(KVATTN_ERR_INVALID, "x, w and y must be 16-byte aligned");
+  const int64_t blocks = (int64_t)outer * heads * ((rows + 127) / 128) * (n_dim / 128);
+  if (blocks > INT32_MAX) return fail(KVATTN_ERR_UNSUPPORTED, "projection of %lld tiles is too large for one launch", blocks);
+  return KVATTN_OK;
+}
+
+kvattn::ProjectArgs project_args(const void* x, const void* w, void* y, int32_t outer, int32_t heads, int32_t rows,
+                                 int32_t k_dim, int32_t n_dim, int64_t xo, int64_t xh, int64_t xr, int64_t wh,
+                                 bool wt, int64_t yo, int64_t yh, int64_t yr) {
+  kvattn::ProjectArgs p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.w = static_cast<const uint16_t*>(w);
+  p.y = static_cast<uint16_t*>(y);
+  p.outer = outer;
+  p.heads = heads;
+  p.rows = rows;
+  p.k_dim = k_dim;
+  p.n_dim = n_dim;
+  p.x_outer = xo;
+  p.x_head = xh;
+  p.x_row = xr;
+  p.w_head = wh;
+  p.y_outer = yo;
+  p.y_head = yh;
+  p.y_row = yr;
+  p.m_tiles = (rows + 127) / 128;
+  p.n_tiles = n_dim / 128;
+  p.w_transposed = wt;
+  return p;
+}
+
 }  // namespace
 
 namespace kvattn {
@@ -484,6 +558,117 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
   if (e != hipSuccess) return hip_status(e, "MLA kernel launch");
   e = kvattn::launch_mla_merge_pieces(a, s);
   if (e != hipSuccess) return hip_status(e, "merge kernel launch");
+  return ok();
+}
+
+kvattn_status kvattn_mla_project(const void* x, const void* w, void* y, int32_t outer, int32_t heads, int32_t rows,
+                                 int32_t k_dim, int32_t n_dim, int64_t x_outer_stride, int64_t x_head_stride,
+                                 int64_t x_row_stride, int64_t w_head_stride, int32_t w_transposed,
+                                 int64_t y_outer_stride, int64_t y_head_stride, int64_t y_row_stride,
+                                 kvattn_dtype dtype, void* stream) {
+  kvattn_status st = check_project(x, w, y, outer, heads, rows, k_dim, n_dim, x_outer_stride, x_head_stride,
+                                   x_row_stride, w_head_stride, y_outer_stride, y_head_stride, y_row_stride, dtype);
+  if (st != KVATTN_OK) return st;
+  if (rows == 0) return ok();
+  const kvattn::ProjectArgs p =
+      project_args(x, w, y, outer, heads, rows, k_dim, n_dim, x_outer_stride, x_head_stride, x_row_stride,
+                   w_head_stride, w_transposed != 0, y_outer_stride, y_head_stride, y_row_stride);
+  const hipError_t e = kvattn::launch_latent_project(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "projection kernel launch");
+  return ok();
+}
+
+size_t kvattn_mla_explicit_workspace_bytes(int32_t batch, int32_t num_heads, int32_t d_head, int32_t d_v,
+                                           int32_t max_seq_len, int32_t split_tokens, kvattn_dtype dtype) {
+  (void)dtype;
+  if (batch < 1 || num_heads < 1 || d_head != kExplicitHead || d_v != kExplicitHead || max_seq_len < 0 ||
+      max_seq_len > kMaxSeqLen || split_tokens < 0 || split_tokens % KVATTN_SPLIT_ALIGN != 0)
+    return (size_t)-1;
+  const int32_t split = plan_gqa_split(batch, num_heads, num_heads, max_seq_len, false, split_tokens);
+  const ExplicitWorkspace w = explicit_workspace(batch, num_heads, max_seq_len, n_splits(max_seq_len, split));
+  return w.total == 0 && max_seq_len > 0 ? (size_t)-1 : w.total;
+}
+
+kvattn_status kvattn_mla_explicit_decode(const void* q, const void* cache, const void* w_uk, const void* w_uv,
+                                         const int32_t* seq_lens, void* out, float* lse, int32_t batch,
+                                         int32_t num_heads, int32_t d_latent, int32_t d_rope, int32_t d_head,
+                                         int32_t d_v, int64_t cache_len, int32_t max_seq_len, float scale,
+                                         kvattn_dtype dtype, int32_t split_tokens, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  const kvattn::LaunchEvents ev = take_timing_events();  // armed for this call only, whatever its outcome
+  if (!q || !cache || !w_uk || !w_uv || !seq_lens || !out)
+    return fail(KVATTN_ERR_INVALID, "q, cache, w_uk, w_uv, seq_lens and out must be non-null");
+  if (batch < 1 || num_heads < 1)
+    return fail(KVATTN_ERR_INVALID, "batch and num_heads must be >= 1 (got %lld, %lld)", batch, num_heads);
+  if (d_latent < 1 || d_rope < 0 || d_head < 1 || d_v < 1)
+    return fail(KVATTN_ERR_INVALID, "bad MLA widths (d_latent=%lld, d_head=%lld)", d_latent, d_head);
+  if (dtype != KVATTN_F32 && dtype != KVATTN_BF16) return fail(KVATTN_ERR_INVALID, "unknown dtype %lld", (int)dtype);
+  if (!std::isfinite(scale)) return fail(KVATTN_ERR_INVALID, "scale must be finite");
+  if (d_latent != kvattn::kMlaLatent || d_rope != kvattn::kMlaRope)
+    return fail(KVATTN_ERR_UNSUPPORTED, "MLA supports d_latent=512, d_rope=64 (got %lld, %lld)", d_latent, d_rope);
+  if (d_head != kExplicitHead || d_v != kExplicitHead)
+    return fail(KVATTN_ERR_UNSUPPORTED, "explicit MLA supports d_head = d_v = 128 (got %lld, %lld)", d_head, d_v);
+  if (dtype != KVATTN_BF16) return fail(KVATTN_ERR_UNSUPPORTED, "MLA supports bf16 only");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(cache) | reinterpret_cast<uintptr_t>(w_uk) |
+       reinterpret_cast<uintptr_t>(w_uv) | reinterpret_cast<uintptr_t>(out)) % 16 != 0)
+    return fail(KVATTN_ERR_INVALID, "q, cache, w_uk, w_uv and out must be 16-byte aligned");
+  kvattn_status st;
+  if ((st = check_cache_geometry(cache_len, 0, 0, max_seq_len, false)) != KVATTN_OK) return st;
+  if ((st = check_split(split_tokens)) != KVATTN_OK) return st;
+  const int32_t split = plan_gqa_split(batch, num_heads, num_heads, max_seq_len, false, split_tokens);
+  const int32_t nsplit = n_splits(max_seq_len, split);
+  const ExplicitWorkspace wl = explicit_workspace(batch, num_heads, max_seq_len, nsplit);
+  if (wl.total == 0 && max_seq_len > 0)
+    return fail(KVATTN_ERR_UNSUPPORTED, "batch %lld x max_seq_len %lld is too large", batch, max_seq_len);
+  if ((int64_t)batch * num_heads * nsplit > INT32_MAX ||
+      (int64_t)batch * num_heads * ((max_seq_len + 127) / 128) > INT32_MAX)
+    return fail(KVATTN_ERR_UNSUPPORTED, "batch %lld x num_heads %lld is too large for one launch", batch, num_heads);
+  if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total))
+    return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)wl.total,
+                workspace == nullptr ? 0 : (long long)workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(KVATTN_ERR_INVALID, "workspace must be 256-byte aligned");
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const int64_t row_elems = kvattn::kMlaRow;
+  const int64_t rec = (int64_t)max_seq_len * kExplicitHead;  // elements of one (sequence, head) block
+  if (max_seq_len > 0) {
+    // k_i = c W_uk^(i) and v_i = c W_uv^(i) for every (sequence, head, row < max_seq_len).
+    kvattn::ProjectArgs p = project_args(cache, w_uk, ws + wl.kc, batch, num_heads, max_seq_len, d_latent,
+                                         kExplicitHead, cache_len * row_elems, 0, row_elems,
+                                         (int64_t)d_latent * kExplicitHead, false, num_heads * rec, rec,
+                                         kExplicitHead);
+    if ((e = kvattn::launch_latent_project(p, s)) != hipSuccess) return hip_status(e, "projection kernel launch");
+    p.w = static_cast<const uint16_t*>(w_uv);
+    p.y = reinterpret_cast<uint16_t*>(ws + wl.v);
+    if ((e = kvattn::launch_latent_project(p, s)) != hipSuccess) return hip_status(e, "projection kernel launch");
+  }
+  kvattn::DecodeArgs a{};
+  a.q = q;
+  a.k = ws + wl.kc;
+  a.v = ws + wl.v;
+  a.rope = cache;
+  a.rec_len = max_seq_len;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.num_q_heads = num_heads;
+  a.num_kv_heads = num_heads;
+  a.group = 1;
+  a.cache_len = cache_len;
+  a.len_cap = max_seq_len;
+  a.window = 0;
+  a.split_tokens = split;
+  a.n_split = nsplit;
+  a.scale_log2 = scale * kvattn::kLog2eHost;
+  if (nsplit > 1) {
+    a.part_o = reinterpret_cast<float*>(ws + wl.part_o);
+    a.part_lse = reinterpret_cast<float*>(ws + wl.part_lse);
+  }
+  if ((e = kvattn::launch_mla_explicit_attend(a, s, ev)) != hipSuccess) return hip_status(e, "attention kernel launch");
+  if (nsplit > 1 && (e = kvattn::launch_merge(a, true, s)) != hipSuccess) return hip_status(e, "merge kernel launch");
   return ok();
 }
 

@@ -57,6 +57,26 @@ struct DecodeArgs {
   const int2* seq_pieces;
   const int32_t* plan_count;
   int32_t max_pieces;       // grid bound: the plan never makes more pieces
+  // Reconstruct-then-attend MLA: k and v hold the reconstructed per-head rows
+  // [B, h, rec_len, 128]; `rope` is the latent cache [B, cache_len, 576],
+  // whose columns 512.. hold the shared RoPE key.
+  const void* rope;
+  int32_t rec_len;
+};
+
+// One batched per-head projection: for outer index o, head i and row m,
+//   y[o, i, m, :] = x[o, i, m, :] W^(i)    (W^(i) [k_dim, n_dim] row-major at w + i * w_head)
+// or, with w_transposed, x W^(i)^T (W^(i) [n_dim, k_dim]).  bf16, strides in elements.
+struct ProjectArgs {
+  const uint16_t* x;
+  const uint16_t* w;
+  uint16_t* y;
+  int32_t outer, heads, rows, k_dim, n_dim;
+  int64_t x_outer, x_head, x_row;
+  int64_t w_head;
+  int64_t y_outer, y_head, y_row;
+  int32_t m_tiles, n_tiles;  // 128-row and 128-column tiles of y
+  bool w_transposed;
 };
 
 // Arguments of the MLA plan kernel.
@@ -103,6 +123,8 @@ hipError_t launch_gqa_fp8(const DecodeArgs& a, hipStream_t stream, const LaunchE
 hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t stream);
 hipError_t launch_mla_merge_pieces(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream);
+hipError_t launch_mla_explicit_attend(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_hbm_read_probe(const void* buf, int64_t n16, uint32_t* sink, int workgroups, hipStream_t stream);
 // Log-sum-exp merge of the per-split GQA partials into out/lse (d_v = 128).
 hipError_t launch_merge(const DecodeArgs& a, bool out_bf16, hipStream_t stream);

@@ -1,0 +1,354 @@
+// Per-head projections between MLA's latent space and the per-head spaces,
+// and the reconstruct-then-attend (non-absorbed) MLA decode built on them.
+//
+// What they compute ("MQA, GQA, and MLA", section 5 "MLA, mechanically";
+// "One dial, four settings", "MLA - compress instead of shrink"): head i
+// rebuilds its keys k_i = c W_uk^(i) and values v_i = c W_uv^(i) from the
+// cached latent c, and attends with its query [q^C_i | q^R_i] over
+// [k_i | k^R]; the decoupled RoPE key k^R is cached beside c and shared by
+// all heads.  That is the naive form the pages contrast with absorption: it
+// turns the latent cache back into one of MHA's size before attending.  The
+// absorbed path instead scores against c directly and applies W_uv once to
+// its latent output, o_i = o_latent_i W_uv^(i): the same projection kernel
+// does that up-projection.
+//
+// latent_project: for every (outer index, head): Y = X W (W stored [K, N]
+// row-major, the layout of c W^(i)) or Y = X W^T (W stored [N, K]), bf16 in,
+// fp32 accumulation, bf16 out, on v_mfma_f32_32x32x16_bf16.  A workgroup (4
+// waves) computes a 128 x 128 tile of Y, each wave a 64 x 64 quadrant, in
+// 64-deep steps of K through a two-stage LDS buffer filled from registers
+// (the next step's loads are in flight while the current step computes).
+// The products are computed transposed, Y^T = W^T X^T, so that each lane
+// holds runs of four consecutive output columns of one row; the tile is
+// staged through LDS and written as whole 128-byte rows.  X tile rows (and
+// [N, K] weight rows) are stored with their 16-byte chunks XOR-swizzled by
+// row; a [K, N] weight tile is stored as 8 column blocks of [64 k][16 cols]
+// and read through the gfx950 transposing LDS read (ds_read_b64_tr_b16),
+// which hands each lane one column and four consecutive k.
+//
+// mla_explicit_attend: attention of one head over its reconstructed rows,
+// one workgroup per (sequence, head, split), on the VALU: a head has no other
+// head sharing its rows, so there is nothing for the matrix cores to reuse.
+// Lanes work in 16-lane groups, one token per group and step, each lane
+// holding 8 of the 128 key dims, 4 of the 64 RoPE dims and 8 of the 128 value
+// dims; the score is reduced across the group with DPP row operations.
+#include <hip/hip_ext.h>
+
+#include "device_common.h"
+#include "kvattn_internal.h"
+
+namespace kvattn {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kRowPitch = kBK * 2;             // bytes per X row (and per [N, K] weight row) in LDS
+constexpr int kXBytes = kBM * kRowPitch;       // 16 KiB
+constexpr int kNbPitch = kBK * 32 + 128;       // [K, N] weight tile: one 16-column block (padded)
+constexpr int kWBytes = 8 * kNbPitch;          // 8 column blocks
+constexpr int kStageBytes = kXBytes + kWBytes;
+constexpr int kStgPitch = 144;                 // output staging row: 64 bf16 + 16 bytes of padding
+
+__device__ __forceinline__ int swz_off(int row, int chunk) { return row * kRowPitch + ((chunk ^ (row & 7)) << 4); }
+
+template <bool kWT>
+__global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;  // quadrant: rows 64*wm.., columns 64*wn..
+  // 1-D grid: column tile fastest, then head, then row tile, then the outer index, so
+  // consecutive workgroups share the X tile.
+  int L = blockIdx.x;
+  const int nt = L % p.n_tiles;
+  L /= p.n_tiles;
+  const int head = L % p.heads;
+  L /= p.heads;
+  const int mt = L % p.m_tiles;
+  const int o = L / p.m_tiles;
+  const int m0 = mt * kBM, n0 = nt * kBN;
+  const uint16_t* x = p.x + (int64_t)o * p.x_outer + (int64_t)head * p.x_head;
+  const uint16_t* w = p.w + (int64_t)head * p.w_head;
+
+  // Loads of K step kt: 1024 16-byte chunks of X and 1024 of W, four of each per thread.
+  u32x4 xr[4], wr[4];
+  auto load = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + 256 * u;
+      const int row = c >> 3, ch = c & 7;
+      xr[u] = u32x4{0u, 0u, 0u, 0u};
+      if (m0 + row < p.rows) xr[u] = *reinterpret_cast<const u32x4*>(x + (int64_t)(m0 + row) * p.x_row + kt * kBK + ch * 8);
+      if constexpr (kWT) {
+        wr[u] = *reinterpret_cast<const u32x4*>(w + (int64_t)(n0 + row) * p.k_dim + kt * kBK + ch * 8);
+      } else {
+        const int k = c >> 4, cc = c & 15;
+        wr[u] = *reinterpret_cast<const u32x4*>(w + (int64_t)(kt * kBK + k) * p.n_dim + n0 + cc * 8);
+      }
+    }
+  };
+  auto store = [&](int stage) __attribute__((always_inline)) {
+    unsigned char* s = lds + stage * kStageBytes;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + 256 * u;
+      const int row = c >> 3, ch = c & 7;
+      *reinterpret_cast<u32x4*>(s + swz_off(row, ch)) = xr[u];
+      if constexpr (kWT) {
+        *reinterpret_cast<u32x4*>(s + kXBytes + swz_off(row, ch)) = wr[u];
+      } else {
+        const int k = c >> 4, cc = c & 15;
+        *reinterpret_cast<u32x4*>(s + kXBytes + (cc >> 1) * kNbPitch + k * 32 + (cc & 1) * 16) = wr[u];
+      }
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[ni][mi][v] = 0.f;
+
+  // Per-lane fragment offsets.  X (B operand of Y^T = W^T X^T): row 32*mi + lane%32 of the
+  // quadrant, chunk 2*kk + lane/32.  W (A operand): column 32*ni + lane%32 with the same k.
+  const int lrow = lane & 31, khalf = lane >> 5;
+  const int G = lane >> 4, n16 = lane & 15;
+  auto compute = [&](int stage) __attribute__((always_inline)) {
+    const unsigned char* s = lds + stage * kStageBytes;
+    const auto* s_lds = (const __attribute__((address_space(3))) unsigned char*)s;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8 xf[2], wf[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int r = 64 * wm + 32 * mi + lrow;
+        xf[mi] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s + swz_off(r, 2 * kk + khalf)));
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        if constexpr (kWT) {
+          const int r = 64 * wn + 32 * ni + lrow;
+          wf[ni] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s + kXBytes + swz_off(r, 2 * kk + khalf)));
+        } else {
+          // Lane n16 of group G receives column 16*(G%2) + n16 of the 32-column block and k =
+          // 16*kk + 8*(G/2) + 0..3 (first read), + 4..7 (second read).
+          const int nb = (64 * wn + 32 * ni + 16 * (G & 1)) >> 4;
+          const int k = 16 * kk + 8 * (G >> 1) + (n16 >> 2);
+          const int off = kXBytes + nb * kNbPitch + k * 32 + 8 * (n16 & 3);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s_lds + off));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(s_lds + off + 4 * 32));
+          wf[ni] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ni], xf[mi], acc[ni][mi], 0, 0, 0);
+    }
+  };
+
+  const int nk = p.k_dim / kBK;
+  load(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    store(kt & 1);
+    __syncthreads();
+    if (kt + 1 < nk) load(kt + 1);
+    compute(kt & 1);
+  }
+
+  // acc[ni][mi][v] = Y[row 32*mi + lane%32][col 32*ni + 8*(v/4) + 4*(lane/32) + v%4] of the quadrant.
+  __syncthreads();  // every wave is done with the operand buffers
+  unsigned char* stg = lds + wave * (64 * kStgPitch);
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r = 32 * mi + lrow, col = 32 * ni + 8 * g4 + 4 * khalf;
+        const f32x16& a = acc[ni][mi];
+        *reinterpret_cast<uint2*>(stg + r * kStgPitch + col * 2) =
+            make_uint2(pack_bf16x2(a[4 * g4], a[4 * g4 + 1]), pack_bf16x2(a[4 * g4 + 2], a[4 * g4 + 3]));
+      }
+  __syncthreads();  // the staged rows have landed
+  uint16_t* y = p.y + (int64_t)o * p.y_outer + (int64_t)head * p.y_head;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int c = lane + 64 * u;
+    const int r = c >> 3, ch = c & 7;
+    const int m = m0 + 64 * wm + r;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStgPitch + ch * 16);
+    if (m < p.rows) *reinterpret_cast<u32x4*>(y + (int64_t)m * p.y_row + n0 + 64 * wn + ch * 8) = v;
+  }
+}
+
+// Sum over the 16 lanes of a row (DPP row operations: swap neighbours, swap pairs, mirror
+// within 8 lanes, mirror within 16); every lane of the row receives the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+constexpr int kExHead = 128;  // reconstructed key (content part) and value width
+constexpr int kExRope = 64;
+constexpr int kExSteps = 4;   // tokens per lane group and loop step
+
+__global__ __launch_bounds__(256) void mla_explicit_attend(DecodeArgs a) {
+  const int L = blockIdx.x;
+  const int split = L % a.n_split;
+  const int row = L / a.n_split;  // b * h + head
+  const int h = a.num_q_heads;
+  const int b = row / h;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tg = lane >> 4, sub = lane & 15;
+
+  const int len = clamp_len(a.seq_lens[b], a.len_cap);
+  const int t_begin = split * a.split_tokens;
+  const bool final_out = a.n_split == 1;
+  if (!final_out && t_begin >= len) return;  // the merge reads only splits that hold tokens
+  const int t_end = min(len, t_begin + a.split_tokens);
+
+  // Query: content dims 8*sub .. +7, RoPE dims 4*sub .. +3.
+  const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t)row * (kExHead + kExRope);
+  const u32x4 qc = *reinterpret_cast<const u32x4*>(qrow + 8 * sub);
+  const uint2 qr = *reinterpret_cast<const uint2*>(qrow + kExHead + 4 * sub);
+
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k) + (int64_t)row * a.rec_len * kExHead + 8 * sub;
+  const uint16_t* vr = static_cast<const uint16_t*>(a.v) + (int64_t)row * a.rec_len * kExHead + 8 * sub;
+  const uint16_t* kr = static_cast<const uint16_t*>(a.rope) + (int64_t)b * a.cache_len * kMlaRow + kMlaLatent + 4 * sub;
+
+  struct Step {
+    u32x4 k[kExSteps], v[kExSteps];
+    uint2 r[kExSteps];
+  };
+  // Tokens of one loop step for this lane's group: t0 + 4u + group (the last valid token stands in past the end).
+  auto fetch = [&](int t0, Step& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kExSteps; ++u) {
+      const int t = min(t0 + 4 * u + tg, t_end - 1);
+      st.k[u] = *reinterpret_cast<const u32x4*>(kc + (int64_t)t * kExHead);
+      st.v[u] = *reinterpret_cast<const u32x4*>(vr + (int64_t)t * kExHead);
+      st.r[u] = *reinterpret_cast<const uint2*>(kr + (int64_t)t * kMlaRow);
+    }
+  };
+
+  float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+  constexpr int kWaveTokens = 4 * kExSteps;  // tokens a wave takes per step
+  Step cur, nxt;
+  int t0 = t_begin + wave * kWaveTokens;
+  if (t0 < t_end) fetch(t0, cur);
+  for (; t0 < t_end; t0 += 4 * kWaveTokens) {
+    const int tn = t0 + 4 * kWaveTokens;
+    if (tn < t_end) fetch(tn, nxt);
+    float s[kExSteps];
+#pragma unroll
+    for (int u = 0; u < kExSteps; ++u) {
+      float d = dot2(qc[0], cur.k[u][0], 0.f);
+      d = dot2(qc[1], cur.k[u][1], d);
+      d = dot2(qc[2], cur.k[u][2], d);
+      d = dot2(qc[3], cur.k[u][3], d);
+      d = dot2(qr.x, cur.r[u].x, d);
+      d = dot2(qr.y, cur.r[u].y, d);
+      s[u] = row16_sum(d) * a.scale_log2;
+      if (t0 + 4 * u + tg >= t_end) s[u] = -INFINITY;
+    }
+    const float m_new = fmaxf(m, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing attended yet: keep the weights at 0
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kExSteps; ++u) {
+      const float pu = fast_exp2(s[u] - m_use);
+      l += pu;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += pu * bf16_lo(cur.v[u][e]);
+        acc[2 * e + 1] += pu * bf16_hi(cur.v[u][e]);
+      }
+    }
+    cur = nxt;
+  }
+
+  // Combine the wave's four lane groups (same dims, different tokens), then the four waves.
+  auto merge_in = [&](float m2, float l2, const float* acc2) __attribute__((always_inline)) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    const float a1 = fast_exp2(m - M), a2 = fast_exp2(m2 - M);
+    l = l * a1 + l2 * a2;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] = acc[d] * a1 + acc2[d] * a2;
+    m = M;
+  };
+#pragma unroll
+  for (int sh = 16; sh <= 32; sh <<= 1) {
+    float o[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] = __shfl_xor(acc[d], sh, 64);
+    const float m2 = __shfl_xor(m, sh, 64), l2 = __shfl_xor(l, sh, 64);
+    merge_in(m2, l2, o);
+  }
+  __shared__ float red[4][16][10];
+  if (lane < 16) {
+    red[wave][sub][0] = m;
+    red[wave][sub][1] = l;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) red[wave][sub][2 + d] = acc[d];
+  }
+  __syncthreads();
+  if (wave != 0 || lane >= 16) return;
+#pragma unroll
+  for (int w2 = 1; w2 < 4; ++w2) merge_in(red[w2][sub][0], red[w2][sub][1], &red[w2][sub][2]);
+
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  const float lse2 = empty ? -INFINITY : m + __log2f(l);
+  const u32x4 packed = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                        pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  if (final_out) {
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + (int64_t)row * kExHead + 8 * sub) = packed;
+    if (a.lse != nullptr && sub == 0) a.lse[row] = lse2 * kLn2;
+  } else {
+    const int64_t prow = (int64_t)row * a.n_split + split;
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.part_o) + prow * kExHead + 8 * sub) = packed;
+    if (sub == 0) a.part_lse[prow] = lse2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.outer * p.heads * p.m_tiles * p.n_tiles;
+  if (blocks <= 0 || blocks > 0x7fffffff || p.k_dim % kBK != 0 || p.n_dim % kBN != 0) return hipErrorInvalidValue;
+  if (p.w_transposed) latent_project<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  else latent_project<false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_explicit_attend(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
+  const int64_t blocks = (int64_t)a.batch * a.num_q_heads * a.n_split;
+  if (blocks <= 0 || blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL(mla_explicit_attend, dim3((unsigned)blocks), dim3(256), 0, stream, ev.start, ev.stop, 0, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvattn

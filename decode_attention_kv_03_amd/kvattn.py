@@ -49,6 +49,17 @@ SIGNATURES = {
          _c_f32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
     ),
     "kvattn_mla_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "kvattn_mla_project": (
+        _c_i32,
+        [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64,
+         _c_i64, _c_i64, _c_i32, _c_vp],
+    ),
+    "kvattn_mla_explicit_decode": (
+        _c_i32,
+        [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+         _c_i32, _c_f32, _c_i32, _c_i32, _c_vp, _c_sz, _c_vp],
+    ),
+    "kvattn_mla_explicit_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_gqa_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_mla_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_time_next_kernel": (_c_i32, [_c_vp, _c_vp]),
@@ -366,5 +377,102 @@ def mla_decode(q, cache, seq_lens, scale, *, block_table=None, max_seq_len=None,
     _check(lib.kvattn_mla_decode(
         _ptr(q), _ptr(cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse), B, h, d_latent, d_rope,
         cache_len, block_size, max_blocks, max_seq_len, float(scale), code, int(split_tokens), _ptr(ws), nbytes,
+        _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def mla_project(x, w, y, *, outer, heads, rows, k_dim, n_dim, x_strides, w_head_stride, y_strides,
+                w_transposed=False, stream=None):
+    """kvattn_mla_project on raw strides: y[o, i, m] = x[o, i, m] W^(i) (or W^(i)^T).
+
+    ``x_strides`` and ``y_strides`` are (outer, head, row) strides in elements;
+    x, w and y are bfloat16 GPU tensors (their data pointers are used as-is).
+    """
+    _need_gpu(x, w, y)
+    for t in (x, w, y):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("kvattn: projections take bfloat16 tensors")
+    lib = load_library()
+    _check(lib.kvattn_mla_project(_ptr(x), _ptr(w), _ptr(y), int(outer), int(heads), int(rows), int(k_dim), int(n_dim),
+                                  *[int(v) for v in x_strides], int(w_head_stride), int(bool(w_transposed)),
+                                  *[int(v) for v in y_strides], KVATTN_BF16, _stream(stream)))
+    return y
+
+
+def mla_up_project(o_latent, w_uv, out=None, stream=None):
+    """Per-head W_uv up-projection of absorbed MLA outputs: o_latent [B, h, d_c] x W_uv [h, d_c, d_v] -> [B, h, d_v]."""
+    B, h, d_c = o_latent.shape
+    if w_uv.dim() != 3 or w_uv.shape[0] != h or w_uv.shape[1] != d_c:
+        raise ValueError("kvattn: w_uv must be [h, d_c, d_v]")
+    d_v = w_uv.shape[2]
+    if out is None:
+        out = torch.empty((B, h, d_v), dtype=o_latent.dtype, device=o_latent.device)
+    elif out.shape != (B, h, d_v):
+        raise ValueError("kvattn: out must be [B, h, d_v]")
+    return mla_project(o_latent, w_uv, out, outer=1, heads=h, rows=B, k_dim=d_c, n_dim=d_v,
+                       x_strides=(0, d_c, h * d_c), w_head_stride=d_c * d_v, y_strides=(0, d_v, h * d_v),
+                       stream=stream)
+
+
+def mla_absorb_query(q_c, w_uk, out=None, stream=None):
+    """Absorbed content queries q^C_i W_uk^(i)^T: q_c [B, h, d_h] with W_uk [h, d_c, d_h] -> [B, h, d_c].
+
+    ``out`` may be a wider [B, h, d_c + d_r] tensor: the result fills its first d_c columns.
+    """
+    B, h, d_h = q_c.shape
+    if w_uk.dim() != 3 or w_uk.shape[0] != h or w_uk.shape[2] != d_h:
+        raise ValueError("kvattn: w_uk must be [h, d_c, d_h]")
+    d_c = w_uk.shape[1]
+    if out is None:
+        out = torch.empty((B, h, d_c), dtype=q_c.dtype, device=q_c.device)
+    if out.dim() != 3 or out.shape[:2] != (B, h) or out.shape[2] < d_c:
+        raise ValueError("kvattn: out must be [B, h, >= d_c]")
+    width = out.shape[2]
+    return mla_project(q_c, w_uk, out, outer=1, heads=h, rows=B, k_dim=d_h, n_dim=d_c,
+                       x_strides=(0, d_h, h * d_h), w_head_stride=d_c * d_h, y_strides=(0, width, h * width),
+                       w_transposed=True, stream=stream)
+
+
+def mla_explicit_workspace_bytes(batch, num_heads, max_seq_len, d_head=128, d_v=128, split_tokens=0):
+    lib = load_library()
+    n = lib.kvattn_mla_explicit_workspace_bytes(batch, num_heads, d_head, d_v, max_seq_len, split_tokens, KVATTN_BF16)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("kvattn: arguments rejected by kvattn_mla_explicit_workspace_bytes")
+    return n
+
+
+def mla_explicit_decode(q, cache, w_uk, w_uv, seq_lens, scale, *, max_seq_len=None, out=None, return_lse=False,
+                        lse=None, split_tokens=0, workspace=None, stream=None, d_latent=512):
+    """Reconstruct-then-attend MLA decode (kvattn_mla_explicit_decode).
+
+    q [B, h, d_h + d_r] rows [q^C | q^R]; cache [B, S, d_latent + d_r]; w_uk [h, d_latent, d_h];
+    w_uv [h, d_latent, d_v].  Returns out [B, h, d_v] (and lse [B, h]).
+    """
+    _need_gpu(q, cache, w_uk, w_uv, seq_lens, out, lse, workspace)
+    if q.dim() != 3 or cache.dim() != 3 or cache.shape[0] != q.shape[0]:
+        raise ValueError("kvattn: q must be [B, h, d_h + d_r] and cache [B, S, d_latent + d_r]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (q.shape[0],):
+        raise ValueError("kvattn: seq_lens must be int32 [B]")
+    B, h, width = q.shape
+    d_rope = cache.shape[2] - d_latent
+    d_head = width - d_rope
+    if w_uk.shape != (h, d_latent, d_head) or w_uv.dim() != 3 or w_uv.shape[:2] != (h, d_latent):
+        raise ValueError("kvattn: w_uk must be [h, d_latent, d_head] and w_uv [h, d_latent, d_v]")
+    d_v = w_uv.shape[2]
+    code = _dtype_code(q)
+    cache_len = cache.shape[1]
+    max_seq_len = cache_len if max_seq_len is None else int(max_seq_len)
+    if out is None:
+        out = torch.empty((B, h, d_v), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, h), dtype=torch.float32, device=q.device)
+    lib = load_library()
+    nbytes = lib.kvattn_mla_explicit_workspace_bytes(B, h, d_head, d_v, max_seq_len, split_tokens, code)
+    if nbytes == ctypes.c_size_t(-1).value:
+        nbytes = 0
+    ws = _workspace(nbytes, workspace, q.device)
+    _check(lib.kvattn_mla_explicit_decode(
+        _ptr(q), _ptr(cache), _ptr(w_uk), _ptr(w_uv), _ptr(seq_lens), _ptr(out), _ptr(lse), B, h, d_latent, d_rope,
+        d_head, d_v, cache_len, max_seq_len, float(scale), code, int(split_tokens), _ptr(ws), nbytes,
         _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out

@@ -60,6 +60,9 @@ class MlaWorkload:
     d_rope: int = 64
     dtype: str = "bf16"
     block_size: int = 0  # 0: contiguous [B, S, d_latent + d_rope]; else pool [num_blocks, block_size, 576]
+    form: str = "absorbed"  # "explicit": per-head query [q^C | q^R] and weights W_uk, W_uv (reconstruct, then attend)
+    d_head: int = 128  # explicit form: per-head content key width (W_uk [h, d_latent, d_head])
+    d_v: int = 128  # explicit form: per-head value width (W_uv [h, d_latent, d_v])
 
     @property
     def paged(self):
@@ -84,6 +87,8 @@ WORKLOADS = {
         # Paged latent cache: 64-token blocks, lengths uniform on [1, 16384], a random block permutation.
         MlaWorkload("deepseek_v2_mla_paged_h128_b32_bs64_len1_16384", 32, 128, 16384, 7, 1 / math.sqrt(192),
                     block_size=64),
+        # The same DeepSeek-V2 layer in the naive form: per-head query and synthetic up-projection weights.
+        MlaWorkload("deepseek_v2_mla_explicit_h128_b32_s8192", 32, 128, 8192, 8, 1 / math.sqrt(192), form="explicit"),
     ]
 }
 
@@ -108,14 +113,15 @@ def _fp8_codes(shape, gen, device, scales, head_dim_axis, chunks=1):
     return out
 
 
-def _randn(shape, gen, device, dtype, chunks=1):
-    """iid N(0,1) drawn in float32 then rounded to ``dtype``; drawn in ``chunks`` slabs along dim 0."""
+def _randn(shape, gen, device, dtype, chunks=1, std=1.0):
+    """iid N(0, std^2) drawn in float32 then rounded to ``dtype``; drawn in ``chunks`` slabs along dim 0."""
     out = torch.empty(shape, dtype=dtype, device=device)
     n0 = shape[0]
     step = max(1, (n0 + chunks - 1) // chunks)
     for a in range(0, n0, step):
         b = min(n0, a + step)
-        out[a:b] = torch.randn((b - a, *shape[1:]), generator=gen, device=device, dtype=torch.float32).to(dtype)
+        x = torch.randn((b - a, *shape[1:]), generator=gen, device=device, dtype=torch.float32)
+        out[a:b] = (x * std if std != 1.0 else x).to(dtype)
     return out
 
 
@@ -216,6 +222,38 @@ def make_mla_inputs(w, device="cpu", lens=None, poison_tail=False):
         "cache": cache,
         "seq_lens": torch.from_numpy(lens_np.astype(np.int32)).to(device),
         "block_table": bt,
+        "workload": w,
+    }
+
+
+def make_mla_explicit_inputs(w, device="cpu", lens=None, poison_tail=False):
+    """Inputs for one reconstruct-then-attend MLA step (contiguous latent cache).
+
+    q [B, h, d_head + d_rope] rows [q^C | q^R] ~ N(0,1); cache [B, S, 576] ~
+    N(0,1); W_uk [h, d_latent, d_head] and W_uv [h, d_latent, d_v] ~
+    N(0, 1/d_latent), so that rebuilt keys and values are ~ N(0,1) per
+    component (and scale 1/sqrt(d_head + d_rope) keeps scores ~ N(0,1)).
+    Drawn in that order, all bfloat16.  The pages give no weights; these are
+    synthetic stand-ins of DeepSeek-V2's shapes.
+    """
+    gen = torch.Generator(device=device).manual_seed(w.seed)
+    dt = torch_dtype(w.dtype)
+    B, h, width = w.batch, w.num_heads, w.d_latent + w.d_rope
+    q = _randn((B, h, w.d_head + w.d_rope), gen, device, dt)
+    lens_np = np.full(B, w.seq_len, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
+    cache = _randn((B, w.seq_len, width), gen, device, dt, chunks=B)
+    std = 1.0 / math.sqrt(w.d_latent)
+    w_uk = _randn((h, w.d_latent, w.d_head), gen, device, dt, std=std)
+    w_uv = _randn((h, w.d_latent, w.d_v), gen, device, dt, std=std)
+    if poison_tail:
+        _poison(cache, None, lens_np, None, 0)
+    return {
+        "q": q,
+        "cache": cache,
+        "w_uk": w_uk,
+        "w_uv": w_uv,
+        "seq_lens": torch.from_numpy(lens_np.astype(np.int32)).to(device),
+        "block_table": None,
         "workload": w,
     }
 

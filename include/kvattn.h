@@ -260,6 +260,77 @@ size_t kvattn_mla_workspace_bytes(int32_t batch, int32_t num_heads, int32_t d_la
                                   int32_t d_rope, int32_t max_seq_len, int32_t block_size,
                                   int32_t split_tokens, kvattn_dtype dtype);
 
+/*
+ * Per-head projection between MLA's latent space and a per-head space, on the
+ * bf16 matrix cores (fp32 accumulation, bf16 result):
+ *
+ *     y[o][i][m][:] = x[o][i][m][:] . W^(i)            (w_transposed == 0)
+ *     y[o][i][m][:] = x[o][i][m][:] . W^(i)^T          (w_transposed != 0)
+ *
+ * for every outer index o < outer, head i < heads and row m < rows.  W^(i)
+ * starts at w + i * w_head_stride and is [k_dim, n_dim] row-major (the
+ * layout of c W^(i) with c a row of k_dim latent values), or [n_dim, k_dim]
+ * when transposed.  Row m of x for (o, i) starts at x + o * x_outer_stride +
+ * i * x_head_stride + m * x_row_stride, and likewise for y; strides are in
+ * elements.  This is the up-projection the absorbed form applies once to its
+ * latent output, o_i = o_latent_i W_uv^(i) ("MQA, GQA, and MLA", section 5
+ * "MLA, mechanically": v_i = c W_uv^(i), whose weights the absorbed form
+ * moves past the attention sum); with x = q^C and W_uk transposed it forms
+ * the absorbed query q^C_i W_uk^(i)^T, and kvattn_mla_explicit_decode uses
+ * it to rebuild keys and values.
+ *
+ *  x, w, y      DEVICE pointers, bf16, 16-byte aligned; y must not overlap x or w.
+ *  Supported:   dtype bf16, k_dim a multiple of 64, n_dim a multiple of 128,
+ *               strides non-negative multiples of 8 elements, x_row_stride >=
+ *               k_dim and y_row_stride >= n_dim (x_head_stride may be 0: one x
+ *               shared by all heads).  rows == 0 enqueues nothing.
+ */
+kvattn_status kvattn_mla_project(const void* x, const void* w, void* y, int32_t outer, int32_t heads, int32_t rows,
+                                 int32_t k_dim, int32_t n_dim, int64_t x_outer_stride, int64_t x_head_stride,
+                                 int64_t x_row_stride, int64_t w_head_stride, int32_t w_transposed,
+                                 int64_t y_outer_stride, int64_t y_head_stride, int64_t y_row_stride,
+                                 kvattn_dtype dtype, void* stream);
+
+/*
+ * Non-absorbed ("reconstruct, then attend") MLA decode: the naive form the
+ * pages set against absorption, which rebuilds per-head keys and values from
+ * the latent cache and so turns it back into a cache of MHA's size before
+ * attending ("One dial, four settings", "MLA - compress instead of shrink";
+ * "MQA, GQA, and MLA", section 5 and exercise D of section 11, where the two
+ * forms must agree).  Head i of sequence b computes
+ *
+ *     k_{i,t} = [c_t W_uk^(i) | k^R_t],   v_{i,t} = c_t W_uv^(i),
+ *     s_t = scale * <[q^C_i | q^R_i], k_{i,t}>,  out_i = sum_t softmax(s)_t v_{i,t}
+ *
+ * over t < seq_lens[b], which equals kvattn_mla_decode on the absorbed query
+ * followed by the W_uv up-projection (kvattn_mla_project), up to rounding.
+ *
+ *  q            [batch, num_heads, d_head + d_rope]: [q^C_i | q^R_i], bf16.
+ *  cache        contiguous latent cache [batch, cache_len, d_latent + d_rope],
+ *               rows [c_t | k^R_t], bf16 (as for kvattn_mla_decode).
+ *  w_uk, w_uv   [num_heads, d_latent, d_head] and [num_heads, d_latent, d_v],
+ *               bf16: k = c W_uk^(i), v = c W_uv^(i).
+ *  out          [batch, num_heads, d_v], bf16; lse NULL or fp32 [batch, num_heads].
+ *  workspace    kvattn_mla_explicit_workspace_bytes() bytes, 256-byte aligned:
+ *               it holds the rebuilt keys (content part) and values,
+ *               [batch, num_heads, max_seq_len, 128] bf16 each, for every row
+ *               below max_seq_len (the naive form rebuilds them all), then the
+ *               split partials.
+ *  Supported: bf16, d_latent 512, d_rope 64, d_head = d_v = 128 (DeepSeek-V2's
+ *  shapes).  The rebuilt rows are rounded to bf16 before attention, one more
+ *  rounding than the absorbed path takes.
+ */
+kvattn_status kvattn_mla_explicit_decode(const void* q, const void* cache, const void* w_uk, const void* w_uv,
+                                         const int32_t* seq_lens, void* out, float* lse, int32_t batch,
+                                         int32_t num_heads, int32_t d_latent, int32_t d_rope, int32_t d_head,
+                                         int32_t d_v, int64_t cache_len, int32_t max_seq_len, float scale,
+                                         kvattn_dtype dtype, int32_t split_tokens, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/* Workspace bytes kvattn_mla_explicit_decode needs; (size_t)-1 if it would reject these sizes. */
+size_t kvattn_mla_explicit_workspace_bytes(int32_t batch, int32_t num_heads, int32_t d_head, int32_t d_v,
+                                           int32_t max_seq_len, int32_t split_tokens, kvattn_dtype dtype);
+
 /* The split size (tokens per split) a call with these arguments uses (block_size 0 for a
  * contiguous cache, as for the workspace queries).  split_tokens = 0 asks for the library's choice:
  * for a contiguous GQA cache the fewest splits that still give every compute unit two resident

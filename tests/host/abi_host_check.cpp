@@ -208,7 +208,76 @@ static void scratch_source() {
   }
 }
 
+// Reconstruct-then-attend MLA: workspace regions inside the queried size, the two projections cover every
+// (sequence, head, row < max_seq_len) with the weights' head stride, and the attention reads what they wrote.
+static void explicit_mla() {
+  const int32_t Bs[] = {1, 3, 32};
+  const int32_t Hs[] = {16, 128};
+  const int32_t Ss[] = {0, 1, 300, 8192};
+  const int32_t splits[] = {0, 64};
+  for (int32_t B : Bs)
+    for (int32_t h : Hs)
+      for (int32_t S : Ss)
+        for (int32_t split : splits) {
+          const size_t ws = kvattn_mla_explicit_workspace_bytes(B, h, 128, 128, S, split, KVATTN_BF16);
+          CHECK(ws != kRejected, "B=%d h=%d S=%d", B, h, S);
+          unsigned char* base = reinterpret_cast<unsigned char*>(1 << 20);
+          stub::last = stub::Record{};
+          const int64_t cache_len = S > 0 ? S : 1;
+          const kvattn_status st =
+              kvattn_mla_explicit_decode(P, P, P, P, PI, P, nullptr, B, h, 512, 64, 128, 128, cache_len, S, 0.07f,
+                                         KVATTN_BF16, split, ws ? base : nullptr, ws, nullptr);
+          CHECK(st == KVATTN_OK, "B=%d h=%d S=%d split=%d: %s", B, h, S, split, kvattn_last_error());
+          if (st != KVATTN_OK) continue;
+          if (ws > 0)
+            CHECK(kvattn_mla_explicit_decode(P, P, P, P, PI, P, nullptr, B, h, 512, 64, 128, 128, cache_len, S, 0.07f,
+                                             KVATTN_BF16, split, base, ws - 1, nullptr) == KVATTN_ERR_WORKSPACE,
+                  "short explicit workspace");
+          const kvattn::DecodeArgs& a = stub::last.args;
+          const int64_t rec = (int64_t)B * h * S * 128 * 2;
+          auto inside = [&](const void* p, int64_t bytes) {
+            const unsigned char* c = static_cast<const unsigned char*>(p);
+            return bytes == 0 || (c >= base && c + bytes <= base + ws);
+          };
+          CHECK(inside(a.k, rec) && inside(a.v, rec), "rebuilt rows outside the workspace");
+          CHECK(static_cast<const unsigned char*>(a.v) >= static_cast<const unsigned char*>(a.k) + rec || rec == 0,
+                "keys and values overlap");
+          if (a.n_split > 1) {
+            CHECK(inside(a.part_o, (int64_t)B * h * a.n_split * 128 * 2), "partials outside");
+            CHECK(inside(a.part_lse, (int64_t)B * h * a.n_split * 4), "lse outside");
+          }
+          CHECK((int64_t)a.n_split * a.split_tokens >= S, "splits do not cover the sequence");
+          CHECK(stub::last.n_projects == (S > 0 ? 2 : 0), "projections %d", stub::last.n_projects);
+          if (S > 0) {
+            const kvattn::ProjectArgs& pk = stub::last.projects[0];
+            CHECK(pk.outer == B && pk.heads == h && pk.rows == S && pk.k_dim == 512 && pk.n_dim == 128, "shape");
+            CHECK(pk.x_row == 576 && pk.x_head == 0 && pk.x_outer == cache_len * 576, "x strides");
+            CHECK(pk.w_head == 512 * 128 && !pk.w_transposed, "w stride");
+            CHECK(pk.y_row == 128 && pk.y_head == (int64_t)S * 128 && pk.y_outer == (int64_t)h * S * 128, "y strides");
+            CHECK(reinterpret_cast<const void*>(pk.y) == a.k && reinterpret_cast<const void*>(stub::last.projects[1].y) == a.v,
+                  "attention reads other rows than the projections wrote");
+            CHECK(pk.m_tiles == (S + 127) / 128 && pk.n_tiles == 1, "tiles");
+          }
+          CHECK(a.rec_len == S && a.rope == P, "rope source");
+        }
+  // projections: rejected shapes and strides
+  auto proj = [&](int32_t k, int32_t n, int64_t xr, int64_t yr, const void* y = P) {
+    return kvattn_mla_project(P, P, const_cast<void*>(y), 1, 4, 10, k, n, 0, k, xr, k * n, 0, 0, n, yr, KVATTN_BF16,
+                              nullptr);
+  };
+  CHECK(proj(512, 128, 512 * 4, 128 * 4) == KVATTN_OK, "%s", kvattn_last_error());
+  CHECK(proj(500, 128, 512 * 4, 128 * 4) == KVATTN_ERR_UNSUPPORTED, "k not a multiple of 64");
+  CHECK(proj(512, 100, 512 * 4, 128 * 4) == KVATTN_ERR_UNSUPPORTED, "n not a multiple of 128");
+  CHECK(proj(512, 128, 100, 128 * 4) == KVATTN_ERR_INVALID, "row stride shorter than a row");
+  CHECK(proj(512, 128, 512 * 4 + 4, 128 * 4) == KVATTN_ERR_INVALID, "stride not a multiple of 8");
+  CHECK(proj(512, 128, 512 * 4, 128 * 4, reinterpret_cast<void*>(24)) == KVATTN_ERR_INVALID, "misaligned y");
+  CHECK(kvattn_mla_project(P, P, P, 1, 4, 10, 512, 128, 0, 512, 2048, 65536, 0, 0, 128, 512, KVATTN_F32, nullptr) ==
+            KVATTN_ERR_UNSUPPORTED,
+        "fp32");
+}
+
 int main() {
+  explicit_mla();
   scratch_source();
   gqa_rejections();
   window_sweep();

@@ -32,6 +32,15 @@ hipError_t launch_mla_merge_pieces(const DecodeArgs&, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_hbm_read_probe(const void*, int64_t, uint32_t*, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t) {
+  stub::last.projects[stub::last.n_projects % 2] = p;
+  ++stub::last.n_projects;
+  ++stub::last.launches;
+  return hipSuccess;
+}
+hipError_t launch_mla_explicit_attend(const DecodeArgs& a, hipStream_t, const LaunchEvents&) {
+  return record("mla_explicit_attend", a);
+}
 hipError_t launch_merge(const DecodeArgs&, bool, hipStream_t) {
   ++stub::last.launches;
   ++stub::last.merges;

@@ -8,6 +8,8 @@ struct Record {
   const char* kernel = nullptr;
   kvattn::DecodeArgs args{};
   kvattn::MlaPlanArgs plan{};
+  kvattn::ProjectArgs projects[2]{};
+  int n_projects = 0;
   int launches = 0;
   int merges = 0;
 };

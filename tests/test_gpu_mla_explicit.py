@@ -1,0 +1,171 @@
+"""GPU parity (through the C ABI) of the MLA projections and of the
+reconstruct-then-attend MLA decode, against the fp64 oracle.
+
+* kvattn_mla_project: the W_uv up-projection of latent outputs (W stored
+  [d_c, d_v]) and the query absorption q^C W_uk^T (W stored [d_c, d_h], used
+  transposed), ragged row counts, outputs inside guard bands; bf16 bar
+  |gpu - ref| <= 2e-2 + 1e-2 |ref|.
+* kvattn_mla_explicit_decode against oracle.mla_explicit_decode_batch at
+  DeepSeek-V2's head shapes (d_c 512, d_R 64, d_h = d_v = 128) on ragged,
+  NaN-poisoned caches, at the bf16 bar.  Its log-sum-exp differs from the
+  exact one mostly through the one extra rounding the naive form takes (the
+  rebuilt keys are stored as bf16): a key component moves by at most 2^-8 of
+  itself, so a score by at most scale * 2^-8 * sum_d |q^C_d k_d| and the lse
+  by at most the largest such shift over the sequence; the test computes that
+  bound from the inputs (plus 1e-3 for fp32 arithmetic).
+* At the full DeepSeek-V2 size: the naive form equals the absorbed one
+  followed by the up-projection (exercise D of "MQA, GQA, and MLA",
+  section 11) on every sequence, and the oracle on sampled sequences.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_03_amd import (mla_absorb_query, mla_decode, mla_explicit_decode, mla_explicit_workspace_bytes,
+                                        mla_up_project)
+from decode_attention_kv_03_amd import workloads as W
+from tests.guard import fenced
+from tests.tolerances import BF16_ATOL, BF16_RTOL
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def setup_module(_):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def note(msg):
+    print(f"\n[gpu-test] {msg}", flush=True)
+
+
+def assert_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    bad = err > BF16_ATOL + BF16_RTOL * np.abs(ref)
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside tolerance, max abs err {err.max():.3e}"
+
+
+def f64(t):
+    return oracle.bf16_bits_to_f64(W.host_view(t))
+
+
+@pytest.mark.parametrize("B,h,d_v", [(5, 16, 128), (300, 8, 256), (32, 128, 128), (1, 1, 128)])
+def test_up_projection_matches_oracle(B, h, d_v):
+    gen = torch.Generator(DEV).manual_seed(B + h)
+    o_lat = torch.randn((B, h, 512), generator=gen, device=DEV).to(torch.bfloat16)
+    w_uv = (torch.randn((h, 512, d_v), generator=gen, device=DEV) / 512 ** 0.5).to(torch.bfloat16)
+    note(f"up-projection B={B} h={h} d_v={d_v}")
+    out = fenced((B, h, d_v), torch.bfloat16)
+    mla_up_project(o_lat, w_uv, out=out.tensor)
+    torch.cuda.synchronize()
+    assert out.bands_intact()
+    ref = oracle.mla_up_project(f64(o_lat), f64(w_uv))
+    assert_close(out.tensor.float().cpu().numpy(), ref, "up-projection")
+
+
+@pytest.mark.parametrize("B,h", [(3, 16), (130, 4), (32, 128)])
+def test_query_absorption_matches_oracle(B, h):
+    gen = torch.Generator(DEV).manual_seed(7 * B + h)
+    q_c = torch.randn((B, h, 128), generator=gen, device=DEV).to(torch.bfloat16)
+    w_uk = (torch.randn((h, 512, 128), generator=gen, device=DEV) / 512 ** 0.5).to(torch.bfloat16)
+    note(f"query absorption B={B} h={h}")
+    # into the first 512 columns of a [B, h, 576] query; the RoPE columns stay as they were
+    q_abs = fenced((B, h, 576), torch.bfloat16)
+    rope = torch.randn((B, h, 64), generator=gen, device=DEV).to(torch.bfloat16)
+    q_abs.tensor[..., 512:] = rope
+    mla_absorb_query(q_c, w_uk, out=q_abs.tensor)
+    torch.cuda.synchronize()
+    assert q_abs.bands_intact()
+    assert torch.equal(q_abs.tensor[..., 512:], rope)
+    qc64, wuk64 = f64(q_c), f64(w_uk)
+    ref = np.stack([oracle.mla_absorb_query(qc64[b], wuk64) for b in range(B)])
+    assert_close(q_abs.tensor[..., :512].float().cpu().numpy(), ref, "absorption")
+
+
+def explicit_reference(x, rows=None):
+    w = x["workload"]
+    rows = list(range(w.batch)) if rows is None else rows
+    lens = W.host_view(x["seq_lens"])[rows]
+    q = W.host_view(x["q"])[rows]
+    cache = np.stack([W.host_view(x["cache"][b]) for b in rows])
+    return oracle.mla_explicit_decode_batch(q, cache, lens, W.host_view(x["w_uk"]), W.host_view(x["w_uv"]), w.scale,
+                                            d_c=w.d_latent, bf16=True)
+
+
+def lse_bound(x, rows):
+    """Largest score shift the bf16 rounding of the rebuilt keys can cause, per (sequence, head)."""
+    w = x["workload"]
+    wuk = f64(x["w_uk"])
+    out = np.zeros((len(rows), w.num_heads))
+    for r, b in enumerate(rows):
+        n = int(W.host_view(x["seq_lens"])[b])
+        if n == 0:
+            continue
+        c = f64(x["cache"][b, :n, : w.d_latent])
+        qc = f64(x["q"][b])[:, : w.d_head]
+        for i in range(w.num_heads):
+            k = c @ wuk[i]
+            out[r, i] = w.scale * 2.0 ** -8 * np.max(np.abs(k) @ np.abs(qc[i]))
+    return out + 1e-3
+
+
+def check_explicit(x, out, lse, rows=None):
+    w = x["workload"]
+    rows = list(range(w.batch)) if rows is None else rows
+    ref, ref_lse = explicit_reference(x, rows)
+    assert_close(out[rows].float().cpu().numpy(), ref, "explicit")
+    got = lse[rows].cpu().numpy()
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    bound = lse_bound(x, rows)
+    assert np.all(np.abs(got[fin] - ref_lse[fin]) <= bound[fin]), np.max(np.abs(got[fin] - ref_lse[fin]) - bound[fin])
+
+
+@pytest.mark.parametrize("B,h,lens,split", [
+    (2, 16, [300, 17], 0),
+    (2, 16, [300, 17], 64),
+    (3, 128, [1000, 1, 129], 0),
+    (3, 8, [0, 64, 65], 64),
+    (1, 128, [2048], 256),
+])
+def test_explicit_decode_matches_oracle(B, h, lens, split):
+    w = W.MlaWorkload(f"explicit_{B}_{h}", B, h, max(lens) + 3, 300 + h + B, 1 / np.sqrt(192), form="explicit")
+    note(f"explicit MLA B={B} h={h} lens={lens} split={split}")
+    x = W.make_mla_explicit_inputs(w, DEV, lens=lens, poison_tail=True)
+    out = fenced((B, h, 128), torch.bfloat16)
+    lse = fenced((B, h), torch.float32)
+    nbytes = mla_explicit_workspace_bytes(B, h, w.seq_len, split_tokens=split)
+    ws = fenced((max(nbytes, 1),), torch.uint8)
+    mla_explicit_decode(x["q"], x["cache"], x["w_uk"], x["w_uv"], x["seq_lens"], w.scale, out=out.tensor,
+                        lse=lse.tensor, split_tokens=split, workspace=ws.tensor)
+    torch.cuda.synchronize()
+    assert out.bands_intact() and lse.bands_intact() and ws.bands_intact()
+    check_explicit(x, out.tensor, lse.tensor)
+
+
+def test_full_size_explicit_equals_absorbed_then_up_projected():
+    w = W.WORKLOADS["deepseek_v2_mla_explicit_h128_b32_s8192"]
+    note(w.name)
+    x = W.make_mla_explicit_inputs(w, DEV)
+    out, lse = mla_explicit_decode(x["q"], x["cache"], x["w_uk"], x["w_uv"], x["seq_lens"], w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    # the absorbed form on the same inputs: q~ = [q^C W_uk^T | q^R], latent decode, then W_uv
+    q_abs = torch.empty((w.batch, w.num_heads, 576), dtype=torch.bfloat16, device=DEV)
+    q_abs[..., 512:] = x["q"][..., 128:]
+    mla_absorb_query(x["q"][..., :128].contiguous(), x["w_uk"], out=q_abs)
+    o_lat, lse_abs = mla_decode(q_abs, x["cache"], x["seq_lens"], w.scale, return_lse=True)
+    o_abs = mla_up_project(o_lat, x["w_uv"])
+    torch.cuda.synchronize()
+    a, b = out.double().cpu().numpy(), o_abs.double().cpu().numpy()
+    # each is within the bf16 bar of the exact result, so they are within twice of each other
+    assert np.all(np.abs(a - b) <= 2 * (BF16_ATOL + BF16_RTOL * np.abs(b)))
+    assert np.abs(lse.cpu().numpy() - lse_abs.cpu().numpy()).max() < 0.05
+    check_explicit(x, out, lse, rows=[0, 31])
+    del x
+    torch.cuda.empty_cache()
