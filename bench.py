@@ -410,6 +410,101 @@ def sweep(torch, stream, names, steps, warmup, headline_name, headline_rates):
     return out
 
 
+def mla_forms(torch, stream, steps, warmup=3):
+    """The absorbed and the naive (reconstruct-then-attend) MLA decode of the DeepSeek-V2-shaped layer, timed
+    on the same inputs and weights ("MQA, GQA, and MLA" section 5 and exercise D; "One dial, four settings",
+    MLA - compress instead of shrink).
+
+    absorbed layer: query absorption (q^C W_uk^T), the latent decode, the W_uv up-projection;
+    explicit: kvattn_mla_explicit_decode (rebuild k_i = c W_uk^(i), v_i = c W_uv^(i) for every head and row,
+    then attend).  Both end in the same per-head outputs [B, h, 128].
+    """
+    import numpy as np
+
+    from decode_attention_kv_03_amd import (mla_absorb_query, mla_decode, mla_explicit_decode,
+                                            mla_explicit_workspace_bytes, mla_up_project, mla_workspace_bytes,
+                                            time_next_kernel)
+    from decode_attention_kv_03_amd import workloads as W
+
+    w = W.WORKLOADS["deepseek_v2_mla_explicit_h128_b32_s8192"]
+    print(f"[bench] MLA forms: {w.name}", file=sys.stderr, flush=True)
+    x = W.make_mla_explicit_inputs(w, "cuda:0")
+    B, h, S, d_c, d_r, d_h, d_v = w.batch, w.num_heads, w.seq_len, w.d_latent, w.d_rope, w.d_head, w.d_v
+    dev = "cuda:0"
+    out_e = torch.empty((B, h, d_v), dtype=torch.bfloat16, device=dev)
+    ws_e = torch.empty(mla_explicit_workspace_bytes(B, h, S), dtype=torch.uint8, device=dev)
+    q_abs = torch.empty((B, h, d_c + d_r), dtype=torch.bfloat16, device=dev)
+    q_abs[..., d_c:] = x["q"][..., d_h:]
+    q_c = x["q"][..., :d_h].contiguous()
+    o_lat = torch.empty((B, h, d_c), dtype=torch.bfloat16, device=dev)
+    out_a = torch.empty((B, h, d_v), dtype=torch.bfloat16, device=dev)
+    ws_a = torch.empty(mla_workspace_bytes(B, h, S), dtype=torch.uint8, device=dev)
+
+    def explicit():
+        mla_explicit_decode(x["q"], x["cache"], x["w_uk"], x["w_uv"], x["seq_lens"], w.scale, out=out_e,
+                            workspace=ws_e, stream=stream)
+
+    def absorbed():
+        mla_absorb_query(q_c, x["w_uk"], out=q_abs, stream=stream)
+        mla_decode(q_abs, x["cache"], x["seq_lens"], w.scale, out=o_lat, workspace=ws_a, stream=stream)
+        mla_up_project(o_lat, x["w_uv"], out=out_a, stream=stream)
+
+    def time(fn, n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for e in evs + kev:
+            e.record(stream)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        for i in range(n):
+            evs[2 * i].record(stream)
+            fn()
+            evs[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(n):
+            time_next_kernel(kev[2 * i], kev[2 * i + 1])
+            fn()
+        torch.cuda.synchronize()
+        call = float(np.mean([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n)])) * 1e3
+        kern = float(np.mean([kev[2 * i].elapsed_time(kev[2 * i + 1]) for i in range(n)])) * 1e3
+        return call, kern
+
+    n = max(3, min(steps, 10))
+    e_call, e_attend = time(explicit, n)
+    a_call, a_decode = time(absorbed, max(n, 20))
+    ntok = B * S
+    rec_flops = 2 * ntok * h * d_c * (d_h + d_v)            # rebuilding keys and values
+    att_flops = 2 * ntok * h * (d_h + d_r + d_v)            # attention over the rebuilt rows
+    rebuilt_bytes = ntok * h * (d_h + d_v) * 2              # rebuilt K and V (written once, read once)
+    latent_bytes = ntok * (d_c + d_r) * 2
+    weight_bytes = 2 * h * d_c * d_h * 2
+    absorbed_flops = 2 * B * h * d_h * d_c + 2 * ntok * h * (2 * d_c + d_r) + 2 * B * h * d_c * d_v
+    recon_us = e_call - e_attend
+    att_read = rebuilt_bytes + ntok * d_r * 2 + B * h * (d_h + d_r + d_v) * 2
+    del ws_e, x
+    torch.cuda.empty_cache()
+    return {
+        "workload": w.name,
+        "explicit_call_us": round(e_call, 1),
+        "explicit_attend_kernel_us": round(e_attend, 1),
+        "explicit_rebuild_us": round(recon_us, 1),
+        "explicit_rebuild_mfma_frac_of_bf16_peak": round(rec_flops / (recon_us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                                                         4),
+        "explicit_attend_hbm_frac": round(att_read / (e_attend * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "explicit_flops": int(rec_flops + att_flops),
+        "explicit_hbm_bytes_min": int(latent_bytes + weight_bytes + 2 * rebuilt_bytes + ntok * d_r * 2),
+        "absorbed_layer_call_us": round(a_call, 1),
+        "absorbed_decode_kernel_us": round(a_decode, 1),
+        "absorbed_flops": int(absorbed_flops),
+        "absorbed_hbm_bytes": int(latent_bytes + weight_bytes + B * h * (d_h + d_r + d_v) * 2),
+        "explicit_over_absorbed_time": round(e_call / a_call, 1),
+        "explicit_over_absorbed_flops": round((rec_flops + att_flops) / absorbed_flops, 1),
+        "rebuilt_bytes_per_token_over_latent": round(h * (d_h + d_v) * 2 / ((d_c + d_r) * 2), 2),
+        "seq_steps_per_s": {"explicit": round(B / (e_call * 1e-6), 1), "absorbed": round(B / (a_call * 1e-6), 1)},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -504,7 +599,8 @@ def main():
         head_rates = dict(head, batch=w.batch, rotated_input_copies=prep.copies)
         del prep
         torch.cuda.empty_cache()
-        all_configs = sweep(torch, stream, SWEEP, args.sweep_steps, 3, w.name, head_rates)
+        all_configs = sweep(torch, stream, SWEEP, args.sweep_steps, 10, w.name, head_rates)
+        all_configs["mla_absorbed_vs_explicit"] = mla_forms(torch, stream, args.sweep_steps)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
