@@ -34,15 +34,35 @@ PROFILES = os.path.join(os.path.dirname(_HERE), "profiles")
 _TAG = re.compile(r"<!-- kvattn-traffic (.*?) -->")
 
 
-def source_sha():
-    """sha256 over the library's kernel and dispatch sources (file names and contents)."""
+# The sources each split-K kernel is compiled and launched from: its own file, the headers it
+# includes, and the dispatch code that plans its splits.
+_COMMON = ["api.cpp", "kvattn_internal.h", "device_common.h", "lds_copy.h", "cache_addr.h"]
+KERNEL_SOURCES = {
+    "gqa_split_bf16": ["gqa_bf16.hip", "gqa_split.h", "merge.hip"] + _COMMON,
+    "gqa_split_fp8": ["gqa_fp8.hip", "gqa_split.h", "merge.hip"] + _COMMON,
+    "gqa_split_f32": ["gqa_f32.hip", "merge.hip"] + _COMMON,
+    "mla_split_bf16": ["mla_bf16.hip", "mla_plan.hip"] + _COMMON,
+}
+
+
+def kernel_of(workload):
+    """The split-K kernel that streams the cache of a named workload."""
+    from . import workloads as W
+
+    w = W.WORKLOADS[workload]
+    return f"gqa_split_{w.dtype}" if hasattr(w, "num_kv_heads") else "mla_split_bf16"
+
+
+def source_sha(kernel=None):
+    """sha256 over the sources a split-K kernel is built and launched from (file names and contents);
+    with no kernel, over every library source."""
     h = hashlib.sha256()
     csrc = os.path.join(_HERE, "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    names = KERNEL_SOURCES[kernel] if kernel else [n for n in os.listdir(csrc) if n.endswith((".hip", ".h", ".cpp"))]
+    for name in sorted(names):
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -89,7 +109,7 @@ def summarize_trace(stats_csv, out_md, title, command):
                     f"{float(r['StdDev']) / 1e3:.2f} |\n")
         other = len(rows) - len(keep)
         f.write(f"\nOther kernels in the trace ({other}) are input generation and copies outside the timed region.\n")
-        f.write(f"\nKernel sources hash: `{source_sha()}`\n")
+        f.write(f"\nLibrary sources hash: `{source_sha()}`\n")
 
 
 def summarize_traffic(workload, out_md, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, commands):
@@ -101,7 +121,8 @@ def summarize_traffic(workload, out_md, fetch_dir, write_dir, copy_fetch_dir, co
     write_scale = copy_bytes / (cwrite_kib * 1024.0)
     fetch_b = fetch_kib * 1024.0 * fetch_scale
     write_b = write_kib * 1024.0 * write_scale
-    sha = source_sha()
+    kernel = kernel_of(workload)
+    sha = source_sha(kernel)
     with open(out_md, "w") as f:
         f.write(f"# HBM traffic of the split-K kernel: {workload}\n\n")
         f.write("rocprofv3 counter runs (one counter per pass), from the repository root on one MI355X:\n\n")
@@ -116,7 +137,7 @@ def summarize_traffic(workload, out_md, fetch_dir, write_dir, copy_fetch_dir, co
         f.write(f"| HBM bytes read per launch (scaled) | {fetch_b:.0f} |\n")
         f.write(f"| HBM bytes written per launch (scaled) | {write_b:.0f} |\n")
         f.write(f"| total traffic per launch | {fetch_b + write_b:.0f} |\n\n")
-        f.write(f"Kernel sources hash: `{sha}`\n\n")
+        f.write(f"Sources hash of `{kernel}` (its file, included headers and dispatch code): `{sha}`\n\n")
         f.write(f"<!-- kvattn-traffic workload={workload} source_sha={sha} fetch_bytes={fetch_b:.0f} "
                 f"write_bytes={write_b:.0f} -->\n")
 
@@ -202,8 +223,8 @@ def summarize_lds(workload, out_md, run_dir, command):
 
 
 def lookup_traffic(workload):
-    """Traffic per split-K launch recorded for `workload` with the current sources, or None."""
-    sha = source_sha()
+    """Traffic per split-K launch recorded for `workload` with the current sources of its kernel, or None."""
+    sha = source_sha(kernel_of(workload))
     for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
         with open(path) as fh:
             for m in _TAG.finditer(fh.read()):

@@ -40,18 +40,28 @@ def test_traffic_summary_scales_counters_and_round_trips_through_the_tag(tmp_pat
                                       (3, MERGE, "FETCH_SIZE", 99999.0, 0, 1)])
     w = _counter_run(tmp_path / "w", [(1, SPLIT, "WRITE_SIZE", 10.0, 0, 1), (2, SPLIT, "WRITE_SIZE", 30.0, 0, 1)])
     out = tmp_path / "x_traffic.md"
-    P.summarize_traffic("some_workload", str(out), str(f), str(w), str(cf), str(cw), copy, "cmd")
+    name = "llama3_8b_gqa_h32_g8_b16_s8192"
+    P.summarize_traffic(name, str(out), str(f), str(w), str(cf), str(cw), copy, "cmd")
     text = out.read_text()
     assert "| HBM bytes read per launch (scaled) | 4096000 |" in text       # 2000 KiB x 1024 x 2
     assert "| HBM bytes written per launch (scaled) | 20480 |" in text      # 20 KiB x 1024 x 1
-    assert f"source_sha={P.source_sha()}" in text
+    sha = P.source_sha("gqa_split_bf16")
+    assert P.kernel_of(name) == "gqa_split_bf16" and f"source_sha={sha}" in text
     monkeypatch.setattr(P, "PROFILES", str(tmp_path))
-    got = P.lookup_traffic("some_workload")
+    got = P.lookup_traffic(name)
     assert got["fetch_bytes"] == 4096000 and got["write_bytes"] == 20480
-    assert P.lookup_traffic("another_workload") is None
-    # A summary taken with other sources is not reported.
-    out.write_text(text.replace(P.source_sha(), "0" * 16))
-    assert P.lookup_traffic("some_workload") is None
+    assert P.lookup_traffic("llama3_70b_gqa_h64_g8_b64_s8192") is None
+    # A summary taken with other sources of the kernel is not reported.
+    out.write_text(text.replace(sha, "0" * 16))
+    assert P.lookup_traffic(name) is None
+
+
+def test_kernel_source_hashes_cover_their_own_sources():
+    # every listed source exists, and the kernels' hashes differ from each other and from the library's
+    shas = {k: P.source_sha(k) for k in P.KERNEL_SOURCES}
+    assert len(set(shas.values())) == len(shas) and P.source_sha() not in shas.values()
+    assert P.kernel_of("deepseek_v2_mla_h128_b32_s8192") == "mla_split_bf16"
+    assert P.kernel_of("llama3_70b_gqa_fp8_h64_g8_b64_s8192") == "gqa_split_fp8"
 
 
 def test_trace_summary_keeps_the_library_kernels(tmp_path):
