@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-all-configs", action="store_true", help="skip the all_configs sweep")
+    p.add_argument("--mla-forms", choices=["both", "explicit", "absorbed"], default=None,
+                   help="only time the absorbed and/or the reconstruct-then-attend MLA layer (one JSON line)")
     p.add_argument("--sweep-steps", type=int, default=20, help="timed calls per workload in the all_configs sweep")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="instead of the workload, run a plain device copy of BYTES bytes --steps times "
@@ -410,7 +412,7 @@ def sweep(torch, stream, names, steps, warmup, headline_name, headline_rates):
     return out
 
 
-def mla_forms(torch, stream, steps, warmup=3):
+def mla_forms(torch, stream, steps, warmup=3, forms="both"):
     """The absorbed and the naive (reconstruct-then-attend) MLA decode of the DeepSeek-V2-shaped layer, timed
     on the same inputs and weights ("MQA, GQA, and MLA" section 5 and exercise D; "One dial, four settings",
     MLA - compress instead of shrink).
@@ -471,8 +473,9 @@ def mla_forms(torch, stream, steps, warmup=3):
         return call, kern
 
     n = max(3, min(steps, 10))
-    e_call, e_attend = time(explicit, n)
-    a_call, a_decode = time(absorbed, max(n, 20))
+    nan = float("nan")
+    e_call, e_attend = time(explicit, n) if forms in ("both", "explicit") else (nan, nan)
+    a_call, a_decode = time(absorbed, max(n, 20)) if forms in ("both", "absorbed") else (nan, nan)
     ntok = B * S
     rec_flops = 2 * ntok * h * d_c * (d_h + d_v)            # rebuilding keys and values
     att_flops = 2 * ntok * h * (d_h + d_r + d_v)            # attention over the rebuilt rows
@@ -525,9 +528,13 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n * 4, "dispatches": args.steps}), flush=True)
         return
 
-    w = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.mla_forms:
+        print(json.dumps({"mla_absorbed_vs_explicit": mla_forms(torch, stream, args.steps, forms=args.mla_forms)}),
+              flush=True)
+        return
+    w = W.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
     prep = Prepared(w, args.split_tokens, stream)
     nbytes, flops = prep.nbytes, prep.flops

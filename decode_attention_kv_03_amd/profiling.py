@@ -3,7 +3,7 @@
     python -m decode_attention_kv_03_amd.profiling trace STATS_CSV OUT_MD TITLE COMMAND
     python -m decode_attention_kv_03_amd.profiling traffic WORKLOAD OUT_MD FETCH_DIR WRITE_DIR \
         COPY_FETCH_DIR COPY_WRITE_DIR COPY_BYTES COMMANDS
-    python -m decode_attention_kv_03_amd.profiling mfma WORKLOAD OUT_MD RUN_DIR TRACE_MD ALGO_FLOPS COMMAND
+    python -m decode_attention_kv_03_amd.profiling mfma WORKLOAD OUT_MD RUN_DIR TRACE_MD ALGO_FLOPS COMMAND [KERNEL]
     python -m decode_attention_kv_03_amd.profiling lds WORKLOAD OUT_MD RUN_DIR COMMAND
 
 ``trace`` condenses a ``--kernel-trace --stats`` kernel_stats.csv into a table
@@ -89,6 +89,13 @@ def _is_split(name):
     return "kvattn" in name and "split" in name
 
 
+def _matcher(kernel):
+    """Dispatch filter: the split-K kernel by default, else library kernels whose name contains `kernel`."""
+    if not kernel:
+        return _is_split
+    return lambda name: "kvattn" in name and kernel in name
+
+
 def _is_copy(name):
     # the device-to-device blit of the copy calibration (not the fill that creates its source)
     return "copybuffer" in name.lower()
@@ -149,13 +156,13 @@ XCDS = 8
 BF16_PEAK_FLOPS = 2.5e15
 
 
-def _trace_split_us(trace_md):
+def _trace_kernel_us(trace_md, match=_is_split):
     with open(trace_md) as fh:
         for line in fh:
             m = re.match(r"\| `(.*?)` \| \d+ \| ([\d.]+) \|", line)
-            if m and _is_split(m.group(1)):
+            if m and match(m.group(1)):
                 return float(m.group(2))
-    raise ValueError(f"no split-K kernel row in {trace_md}")
+    raise ValueError(f"no matching kernel row in {trace_md}")
 
 
 def _mean_dispatch_ns(run_dir, match):
@@ -167,21 +174,23 @@ def _mean_dispatch_ns(run_dir, match):
     return sum(seen.values()) / len(seen)
 
 
-def summarize_mfma(workload, out_md, run_dir, trace_md, algo_flops, command):
-    flops, n = _mean_counter(run_dir, "MfmaFlopsBF16", _is_split)
-    util, _ = _mean_counter(run_dir, "MfmaUtil", _is_split)
-    gui, _ = _mean_counter(run_dir, "GRBM_GUI_ACTIVE", _is_split)
-    run_ns = _mean_dispatch_ns(run_dir, _is_split)
-    us = _trace_split_us(trace_md)
+def summarize_mfma(workload, out_md, run_dir, trace_md, algo_flops, command, kernel=None):
+    match = _matcher(kernel)
+    flops, n = _mean_counter(run_dir, "MfmaFlopsBF16", match)
+    util, _ = _mean_counter(run_dir, "MfmaUtil", match)
+    gui, _ = _mean_counter(run_dir, "GRBM_GUI_ACTIVE", match)
+    run_ns = _mean_dispatch_ns(run_dir, match)
+    us = _trace_kernel_us(trace_md, match)
     # GRBM_GUI_ACTIVE counts the clocks the GPU was busy during the dispatch, and the
     # collection sums it over the XCDs (each has its own GRBM; the MfmaUtil expression
     # takes their maximum instead), so one XCD's clocks are the sum / 8.
     clk = gui / XCDS / (run_ns * 1e-9)
     at_clock = algo_flops / (us * 1e-6) / (CUS * BF16_FLOP_PER_CLK_PER_CU * clk)
     with open(out_md, "w") as f:
-        f.write(f"# Matrix-core counters of the split-K kernel: {workload}\n\n")
+        what = f"`{kernel}`" if kernel else "the split-K kernel"
+        f.write(f"# Matrix-core counters of {what}: {workload}\n\n")
         f.write("rocprofv3 counter run, from the repository root on one MI355X (the kernel's mean duration is\n"
-                f"the split-K row of `{os.path.relpath(trace_md, os.path.dirname(PROFILES))}`):\n\n")
+                f"its row of `{os.path.relpath(trace_md, os.path.dirname(PROFILES))}`):\n\n")
         f.write("```\n" + command + "\n```\n\n")
         f.write("| quantity | value |\n|---|---|\n")
         f.write(f"| MfmaFlopsBF16 per dispatch (GFLOP, mean of {n}) | {flops / 1e9:.3f} |\n")
@@ -249,7 +258,7 @@ def main(argv):
         print(open(argv[2]).read())
         return 0
     if len(argv) >= 7 and argv[0] == "mfma":
-        summarize_mfma(argv[1], argv[2], argv[3], argv[4], float(argv[5]), argv[6])
+        summarize_mfma(argv[1], argv[2], argv[3], argv[4], float(argv[5]), argv[6], argv[7] if len(argv) > 7 else None)
         print(open(argv[2]).read())
         return 0
     print(__doc__, file=sys.stderr)

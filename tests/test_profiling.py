@@ -78,7 +78,7 @@ def test_trace_summary_keeps_the_library_kernels(tmp_path):
     text = out.read_text()
     assert f"| `{SPLIT}` | 30 | 83.28 | 80.00 | 90.00 | 1.50 |" in text
     assert "elementwise_kernel" not in text
-    assert P._trace_split_us(str(out)) == pytest.approx(83.28)
+    assert P._trace_kernel_us(str(out)) == pytest.approx(83.28)
 
 
 def test_mfma_summary_clock_and_utilisation(tmp_path):
