@@ -473,7 +473,7 @@ def mla_forms(torch, stream, steps, warmup=3, forms="both"):
         return call, kern
 
     n = max(3, min(steps, 10))
-    nan = float("nan")
+    nan = float("nan")  # a form not timed in this run (reported as null)
     e_call, e_attend = time(explicit, n) if forms in ("both", "explicit") else (nan, nan)
     a_call, a_decode = time(absorbed, max(n, 20)) if forms in ("both", "absorbed") else (nan, nan)
     ntok = B * S
@@ -487,7 +487,7 @@ def mla_forms(torch, stream, steps, warmup=3, forms="both"):
     att_read = rebuilt_bytes + ntok * d_r * 2 + B * h * (d_h + d_r + d_v) * 2
     del ws_e, x
     torch.cuda.empty_cache()
-    return {
+    out = {
         "workload": w.name,
         "explicit_call_us": round(e_call, 1),
         "explicit_attend_kernel_us": round(e_attend, 1),
@@ -506,6 +506,13 @@ def mla_forms(torch, stream, steps, warmup=3, forms="both"):
         "rebuilt_bytes_per_token_over_latent": round(h * (d_h + d_v) * 2 / ((d_c + d_r) * 2), 2),
         "seq_steps_per_s": {"explicit": round(B / (e_call * 1e-6), 1), "absorbed": round(B / (a_call * 1e-6), 1)},
     }
+
+    def clean(v):
+        if isinstance(v, dict):
+            return {k: clean(x) for k, x in v.items()}
+        return None if isinstance(v, float) and math.isnan(v) else v
+
+    return clean(out)
 
 
 def main():

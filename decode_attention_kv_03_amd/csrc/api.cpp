@@ -14,8 +14,11 @@
 #include "../../include/kvattn.h"
 #include "../../include/kvattn_measure.h"
 #include "kvattn_internal.h"
+#include "plan.h"
 
 namespace {
+
+using namespace kvattn::plan;
 
 thread_local std::string g_last_error;
 // Events the next decode call on this thread records around its split-K kernel.
@@ -39,61 +42,7 @@ kvattn_status ok() {
   return KVATTN_OK;
 }
 
-int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-constexpr int kCUs = 256;          // MI355X compute units
-// Longest sequence a call takes: token indices, split ends and piece ends stay
-// well inside 32-bit arithmetic on the device.
-constexpr int32_t kMaxSeqLen = 1 << 28;
 constexpr int32_t kMaxGridYZ = 65535;  // largest y/z grid dimension the launches use
-
-// Tokens per split for GQA.  A contiguous cache is taken to hold sequences of
-// similar length: the fewest splits that still give every CU two resident
-// workgroups (longer splits amortise each workgroup's start-up and need fewer
-// partials; measured best on all four contiguous workloads).  A paged cache
-// is taken to hold ragged lengths: about four workgroups per CU in all, each
-// at most 2048 tokens, so that long sequences do not leave a tail.
-int32_t plan_gqa_split(int32_t batch, int32_t h, int32_t g, int32_t max_seq_len, bool paged, int32_t requested) {
-  const int64_t S = max_seq_len > 0 ? max_seq_len : 1;
-  // A requested split longer than the longest sequence is one split either way.
-  if (requested > 0) return (int32_t)std::min<int64_t>(requested, round_up(S, KVATTN_SPLIT_ALIGN));
-  const int64_t units = (int64_t)batch * g;
-  const int64_t r = h / g;
-  const int64_t min_chunk = std::max<int64_t>(256, 16 * r);
-  int64_t chunk;
-  if (paged) {
-    chunk = round_up((S * units + 4 * kCUs - 1) / (4 * kCUs), KVATTN_SPLIT_ALIGN);
-    chunk = std::min<int64_t>(std::max(chunk, min_chunk), 2048);
-  } else {
-    const int64_t want_splits = std::max<int64_t>(1, (2 * kCUs + units - 1) / units);
-    chunk = std::max(round_up((S + want_splits - 1) / want_splits, KVATTN_SPLIT_ALIGN), min_chunk);
-  }
-  return (int32_t)std::min(chunk, round_up(S, KVATTN_SPLIT_ALIGN));
-}
-
-// MLA work plan.  The decode kernel's workgroups take pieces of the
-// sequences, cut on the device from the actual lengths (mla_plan.hip): the
-// shortest piece length (a multiple of 32, at least kMlaMinChunk) that gives
-// at most max(kCUs, batch) pieces (one 128-head workgroup fills a CU), or the
-// caller's split_tokens.  The host only bounds the number of pieces.
-constexpr int32_t kMlaMinChunk = 256;
-
-// Piece length the plan chooses when every sequence holds max_seq_len tokens.
-int32_t plan_mla_split(int32_t batch, int32_t max_seq_len, int32_t requested) {
-  if (requested > 0) return requested;
-  const int64_t S = std::max<int32_t>(max_seq_len, 1);
-  const int64_t per_seq = std::max<int64_t>(kCUs, batch) / batch;  // pieces each sequence may take
-  const int64_t t = round_up((S + per_seq - 1) / per_seq, 32);
-  return (int32_t)std::min<int64_t>(std::max<int64_t>(t, kMlaMinChunk), INT32_MAX);
-}
-
-// Upper bound on the number of pieces, or -1 if it overflows.
-int64_t mla_max_pieces(int32_t batch, int32_t max_seq_len, int32_t requested) {
-  const int64_t S = std::max<int32_t>(max_seq_len, 1);
-  const int64_t n = requested > 0 ? (int64_t)batch * ((S + requested - 1) / requested)
-                                  : std::max<int64_t>(kCUs, batch);
-  return n > (int64_t)INT32_MAX / 8 ? -1 : n;
-}
 
 // Workspace regions of an MLA call: partial outputs (bf16), partial log-sum-exps (fp32), the plan's pieces,
 // per-sequence piece ranges and the plan's counts, each 256-byte aligned.
@@ -111,10 +60,6 @@ MlaWorkspace mla_workspace(int64_t batch, int64_t heads, int64_t max_pieces, int
   return w;
 }
 
-int32_t n_splits(int32_t max_seq_len, int32_t split) {
-  if (max_seq_len <= split) return 1;
-  return (int32_t)(((int64_t)max_seq_len + split - 1) / split);
-}
 
 // Split-K partials: outputs of `part_elem` bytes per element, then one fp32 log-sum-exp per row.
 size_t partial_bytes(int64_t batch, int64_t heads, int64_t nsplit, int64_t d_v, int64_t part_elem = 4) {
@@ -304,28 +249,33 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   return ok();
 }
 
-// Reconstruct-then-attend MLA: per-head K and V rows rebuilt from the latent
-// cache ([B, h, max_seq_len, 128] bf16 each), then the split partials (bf16
-// outputs, fp32 log-sum-exps), each region 256-byte aligned.  Sizes in
-// 128-bit arithmetic; total 0 when they overflow (the caller rejects it).
+// Reconstruct-then-attend MLA: the two weights transposed ([h, 128, 512] bf16
+// each, so that the projections read both operands row-wise), per-head K and
+// V rows rebuilt from the latent cache ([B, h, max_seq_len, 128] bf16 each),
+// then the split partials (bf16 outputs, fp32 log-sum-exps), each region
+// 256-byte aligned.  Sizes in 128-bit arithmetic; total 0 when they overflow
+// (the caller rejects it).
 struct ExplicitWorkspace {
-  size_t kc, v, part_o, part_lse, total;
+  size_t wt_k, wt_v, kc, v, part_o, part_lse, total;
 };
 constexpr int32_t kExplicitHead = 128;  // reconstructed content-key and value width
 ExplicitWorkspace explicit_workspace(int64_t batch, int64_t heads, int64_t max_seq_len, int64_t nsplit) {
   typedef unsigned __int128 u128;
   auto up = [](u128 x) { return (x + 255) / 256 * 256; };
+  const u128 wt = up((u128)heads * kvattn::kMlaLatent * kExplicitHead * 2);
   const u128 rows = (u128)batch * heads * (u128)max_seq_len;
   const u128 rec = up(rows * kExplicitHead * 2);
   const u128 po = nsplit > 1 ? up((u128)batch * heads * nsplit * kExplicitHead * 2) : 0;
   const u128 pl = nsplit > 1 ? up((u128)batch * heads * nsplit * 4) : 0;
-  const u128 total = 2 * rec + po + pl;
+  const u128 total = 2 * wt + 2 * rec + po + pl;
   ExplicitWorkspace w{};
   if (total >= ((u128)1 << 56)) return w;
-  w.kc = 0;
-  w.v = (size_t)rec;
-  w.part_o = (size_t)(2 * rec);
-  w.part_lse = (size_t)(2 * rec + po);
+  w.wt_k = 0;
+  w.wt_v = (size_t)wt;
+  w.kc = (size_t)(2 * wt);
+  w.v = (size_t)(2 * wt + rec);
+  w.part_o = (size_t)(2 * wt + 2 * rec);
+  w.part_lse = (size_t)(2 * wt + 2 * rec + po);
   w.total = (size_t)total;
   return w;
 }
@@ -586,7 +536,7 @@ size_t kvattn_mla_explicit_workspace_bytes(int32_t batch, int32_t num_heads, int
     return (size_t)-1;
   const int32_t split = plan_gqa_split(batch, num_heads, num_heads, max_seq_len, false, split_tokens);
   const ExplicitWorkspace w = explicit_workspace(batch, num_heads, max_seq_len, n_splits(max_seq_len, split));
-  return w.total == 0 && max_seq_len > 0 ? (size_t)-1 : w.total;
+  return w.total == 0 ? (size_t)-1 : w.total;
 }
 
 kvattn_status kvattn_mla_explicit_decode(const void* q, const void* cache, const void* w_uk, const void* w_uv,
@@ -618,12 +568,11 @@ kvattn_status kvattn_mla_explicit_decode(const void* q, const void* cache, const
   const int32_t split = plan_gqa_split(batch, num_heads, num_heads, max_seq_len, false, split_tokens);
   const int32_t nsplit = n_splits(max_seq_len, split);
   const ExplicitWorkspace wl = explicit_workspace(batch, num_heads, max_seq_len, nsplit);
-  if (wl.total == 0 && max_seq_len > 0)
-    return fail(KVATTN_ERR_UNSUPPORTED, "batch %lld x max_seq_len %lld is too large", batch, max_seq_len);
+  if (wl.total == 0) return fail(KVATTN_ERR_UNSUPPORTED, "batch %lld x max_seq_len %lld is too large", batch, max_seq_len);
   if ((int64_t)batch * num_heads * nsplit > INT32_MAX ||
       (int64_t)batch * num_heads * ((max_seq_len + 127) / 128) > INT32_MAX)
     return fail(KVATTN_ERR_UNSUPPORTED, "batch %lld x num_heads %lld is too large for one launch", batch, num_heads);
-  if (wl.total > 0 && (workspace == nullptr || workspace_bytes < wl.total))
+  if (workspace == nullptr || workspace_bytes < wl.total)
     return fail(KVATTN_ERR_WORKSPACE, "workspace of %lld bytes needed, %lld given", (long long)wl.total,
                 workspace == nullptr ? 0 : (long long)workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
@@ -634,13 +583,17 @@ kvattn_status kvattn_mla_explicit_decode(const void* q, const void* cache, const
   const int64_t row_elems = kvattn::kMlaRow;
   const int64_t rec = (int64_t)max_seq_len * kExplicitHead;  // elements of one (sequence, head) block
   if (max_seq_len > 0) {
-    // k_i = c W_uk^(i) and v_i = c W_uv^(i) for every (sequence, head, row < max_seq_len).
-    kvattn::ProjectArgs p = project_args(cache, w_uk, ws + wl.kc, batch, num_heads, max_seq_len, d_latent,
+    // k_i = c W_uk^(i) and v_i = c W_uv^(i) for every (sequence, head, row < max_seq_len), with the
+    // weights first transposed to [h, 128, 512] so that both operands are read row-wise.
+    if ((e = kvattn::launch_transpose_heads(w_uk, ws + wl.wt_k, num_heads, d_latent, kExplicitHead, s)) != hipSuccess ||
+        (e = kvattn::launch_transpose_heads(w_uv, ws + wl.wt_v, num_heads, d_latent, kExplicitHead, s)) != hipSuccess)
+      return hip_status(e, "transpose kernel launch");
+    kvattn::ProjectArgs p = project_args(cache, ws + wl.wt_k, ws + wl.kc, batch, num_heads, max_seq_len, d_latent,
                                          kExplicitHead, cache_len * row_elems, 0, row_elems,
-                                         (int64_t)d_latent * kExplicitHead, false, num_heads * rec, rec,
+                                         (int64_t)d_latent * kExplicitHead, true, num_heads * rec, rec,
                                          kExplicitHead);
     if ((e = kvattn::launch_latent_project(p, s)) != hipSuccess) return hip_status(e, "projection kernel launch");
-    p.w = static_cast<const uint16_t*>(w_uv);
+    p.w = reinterpret_cast<const uint16_t*>(ws + wl.wt_v);
     p.y = reinterpret_cast<uint16_t*>(ws + wl.v);
     if ((e = kvattn::launch_latent_project(p, s)) != hipSuccess) return hip_status(e, "projection kernel launch");
   }

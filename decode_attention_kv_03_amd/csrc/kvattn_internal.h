@@ -125,6 +125,8 @@ hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t stream);
 hipError_t launch_mla_merge_pieces(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream);
 hipError_t launch_mla_explicit_attend(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
+// W^(i) [rows, cols] -> W^(i)^T [cols, rows] for every head (bf16; rows, cols multiples of 64).
+hipError_t launch_transpose_heads(const void* src, void* dst, int heads, int rows, int cols, hipStream_t stream);
 hipError_t launch_hbm_read_probe(const void* buf, int64_t n16, uint32_t* sink, int workgroups, hipStream_t stream);
 // Log-sum-exp merge of the per-split GQA partials into out/lse (d_v = 128).
 hipError_t launch_merge(const DecodeArgs& a, bool out_bf16, hipStream_t stream);

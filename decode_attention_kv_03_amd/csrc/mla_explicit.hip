@@ -17,12 +17,12 @@
 // fp32 accumulation, bf16 out, on v_mfma_f32_32x32x16_bf16.  A workgroup (4
 // waves) computes a 128 x 128 tile of Y, each wave a 64 x 64 quadrant, in
 // 64-deep steps of K through a two-stage LDS buffer filled from registers
-// (the next step's loads are in flight while the current step computes).
+// (the loads of two steps ahead are in flight while a step computes).
 // The products are computed transposed, Y^T = W^T X^T, so that each lane
 // holds runs of four consecutive output columns of one row; the tile is
 // staged through LDS and written as whole 128-byte rows.  X tile rows (and
 // [N, K] weight rows) are stored with their 16-byte chunks XOR-swizzled by
-// row; a [K, N] weight tile is stored as 8 column blocks of [64 k][16 cols]
+// row pair; a [K, N] weight tile is stored as 8 column blocks of [64 k][16 cols]
 // and read through the gfx950 transposing LDS read (ds_read_b64_tr_b16),
 // which hands each lane one column and four consecutive k.
 //
@@ -50,7 +50,13 @@ constexpr int kWBytes = 8 * kNbPitch;          // 8 column blocks
 constexpr int kStageBytes = kXBytes + kWBytes;
 constexpr int kStgPitch = 144;                 // output staging row: 64 bf16 + 16 bytes of padding
 
-__device__ __forceinline__ int swz_off(int row, int chunk) { return row * kRowPitch + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk `chunk` of row `row` in a tile of 128-byte rows.  Two rows
+// share one 256-byte line of the 64 banks, so the chunk index is XORed with
+// (row / 2) % 8: any 16 consecutive rows read at one logical chunk (a
+// fragment read's 16-lane group) then land on 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int swz_off(int row, int chunk) {
+  return row * kRowPitch + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
 
 template <bool kWT>
 __global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
@@ -71,35 +77,38 @@ __global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
   const uint16_t* x = p.x + (int64_t)o * p.x_outer + (int64_t)head * p.x_head;
   const uint16_t* w = p.w + (int64_t)head * p.w_head;
 
-  // Loads of K step kt: 1024 16-byte chunks of X and 1024 of W, four of each per thread.
-  u32x4 xr[4], wr[4];
-  auto load = [&](int kt) __attribute__((always_inline)) {
+  // Loads of K step kt: 1024 16-byte chunks of X and 1024 of W, four of each
+  // per thread, into register set `set`; two sets, so the loads of step kt+2
+  // are in flight while step kt computes.
+  u32x4 xr[1][4], wr[1][4];
+  auto load = [&](int kt, int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + 256 * u;
       const int row = c >> 3, ch = c & 7;
-      xr[u] = u32x4{0u, 0u, 0u, 0u};
-      if (m0 + row < p.rows) xr[u] = *reinterpret_cast<const u32x4*>(x + (int64_t)(m0 + row) * p.x_row + kt * kBK + ch * 8);
+      xr[set][u] = u32x4{0u, 0u, 0u, 0u};
+      if (m0 + row < p.rows)
+        xr[set][u] = *reinterpret_cast<const u32x4*>(x + (int64_t)(m0 + row) * p.x_row + kt * kBK + ch * 8);
       if constexpr (kWT) {
-        wr[u] = *reinterpret_cast<const u32x4*>(w + (int64_t)(n0 + row) * p.k_dim + kt * kBK + ch * 8);
+        wr[set][u] = *reinterpret_cast<const u32x4*>(w + (int64_t)(n0 + row) * p.k_dim + kt * kBK + ch * 8);
       } else {
         const int k = c >> 4, cc = c & 15;
-        wr[u] = *reinterpret_cast<const u32x4*>(w + (int64_t)(kt * kBK + k) * p.n_dim + n0 + cc * 8);
+        wr[set][u] = *reinterpret_cast<const u32x4*>(w + (int64_t)(kt * kBK + k) * p.n_dim + n0 + cc * 8);
       }
     }
   };
-  auto store = [&](int stage) __attribute__((always_inline)) {
+  auto store = [&](int stage, int set) __attribute__((always_inline)) {
     unsigned char* s = lds + stage * kStageBytes;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = tid + 256 * u;
       const int row = c >> 3, ch = c & 7;
-      *reinterpret_cast<u32x4*>(s + swz_off(row, ch)) = xr[u];
+      *reinterpret_cast<u32x4*>(s + swz_off(row, ch)) = xr[set][u];
       if constexpr (kWT) {
-        *reinterpret_cast<u32x4*>(s + kXBytes + swz_off(row, ch)) = wr[u];
+        *reinterpret_cast<u32x4*>(s + kXBytes + swz_off(row, ch)) = wr[set][u];
       } else {
         const int k = c >> 4, cc = c & 15;
-        *reinterpret_cast<u32x4*>(s + kXBytes + (cc >> 1) * kNbPitch + k * 32 + (cc & 1) * 16) = wr[u];
+        *reinterpret_cast<u32x4*>(s + kXBytes + (cc >> 1) * kNbPitch + k * 32 + (cc & 1) * 16) = wr[set][u];
       }
     }
   };
@@ -152,11 +161,13 @@ __global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
   };
 
   const int nk = p.k_dim / kBK;
-  load(0);
+  load(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    store(kt & 1);
+    // Stage kt&1 was last read by step kt-2, which every wave finished before
+    // the barrier of step kt-1.
+    store(kt & 1, 0);
     __syncthreads();
-    if (kt + 1 < nk) load(kt + 1);
+    if (kt + 1 < nk) load(kt + 1, 0);
     compute(kt & 1);
   }
 
@@ -183,6 +194,35 @@ __global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
     const int m = m0 + 64 * wm + r;
     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStgPitch + ch * 16);
     if (m < p.rows) *reinterpret_cast<u32x4*>(y + (int64_t)m * p.y_row + n0 + 64 * wn + ch * 8) = v;
+  }
+}
+
+// W^(i) [rows, cols] -> W^(i)^T [cols, rows] for every head, through a
+// 64 x 64 LDS tile (bf16; rows and cols multiples of 64).
+__global__ __launch_bounds__(256) void transpose_heads(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                       int rows, int cols) {
+  __shared__ uint16_t t[64][65];
+  const int tiles_c = cols / 64, tiles_r = rows / 64;
+  int L = blockIdx.x;
+  const int tc = L % tiles_c;
+  L /= tiles_c;
+  const int tr = L % tiles_r;
+  const int head = L / tiles_r;
+  const uint16_t* s = src + (int64_t)head * rows * cols;
+  uint16_t* d = dst + (int64_t)head * rows * cols;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e >> 6, c = e & 63;
+    t[r][c] = s[(int64_t)(64 * tr + r) * cols + 64 * tc + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = tid + 256 * u;
+    const int c = e >> 6, r = e & 63;
+    d[(int64_t)(64 * tc + c) * rows + 64 * tr + r] = t[r][c];
   }
 }
 
@@ -341,6 +381,14 @@ hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream) {
   if (blocks <= 0 || blocks > 0x7fffffff || p.k_dim % kBK != 0 || p.n_dim % kBN != 0) return hipErrorInvalidValue;
   if (p.w_transposed) latent_project<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
   else latent_project<false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_heads(const void* src, void* dst, int heads, int rows, int cols, hipStream_t stream) {
+  if (rows % 64 != 0 || cols % 64 != 0) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)heads * (rows / 64) * (cols / 64);
+  transpose_heads<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(static_cast<const uint16_t*>(src),
+                                                                   static_cast<uint16_t*>(dst), rows, cols);
   return hipGetLastError();
 }
 

@@ -35,8 +35,8 @@ _TAG = re.compile(r"<!-- kvattn-traffic (.*?) -->")
 
 
 # The sources each split-K kernel is compiled and launched from: its own file, the headers it
-# includes, and the dispatch code that plans its splits.
-_COMMON = ["api.cpp", "kvattn_internal.h", "device_common.h", "lds_copy.h", "cache_addr.h"]
+# includes, and the split planning that sets its grid.
+_COMMON = ["plan.h", "kvattn_internal.h", "device_common.h", "lds_copy.h", "cache_addr.h"]
 KERNEL_SOURCES = {
     "gqa_split_bf16": ["gqa_bf16.hip", "gqa_split.h", "merge.hip"] + _COMMON,
     "gqa_split_fp8": ["gqa_fp8.hip", "gqa_split.h", "merge.hip"] + _COMMON,
@@ -144,7 +144,7 @@ def summarize_traffic(workload, out_md, fetch_dir, write_dir, copy_fetch_dir, co
         f.write(f"| HBM bytes read per launch (scaled) | {fetch_b:.0f} |\n")
         f.write(f"| HBM bytes written per launch (scaled) | {write_b:.0f} |\n")
         f.write(f"| total traffic per launch | {fetch_b + write_b:.0f} |\n\n")
-        f.write(f"Sources hash of `{kernel}` (its file, included headers and dispatch code): `{sha}`\n\n")
+        f.write(f"Sources hash of `{kernel}` (its file, included headers and split planning): `{sha}`\n\n")
         f.write(f"<!-- kvattn-traffic workload={workload} source_sha={sha} fetch_bytes={fetch_b:.0f} "
                 f"write_bytes={write_b:.0f} -->\n")
 

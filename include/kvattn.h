@@ -312,7 +312,8 @@ kvattn_status kvattn_mla_project(const void* x, const void* w, void* y, int32_t 
  *               bf16: k = c W_uk^(i), v = c W_uv^(i).
  *  out          [batch, num_heads, d_v], bf16; lse NULL or fp32 [batch, num_heads].
  *  workspace    kvattn_mla_explicit_workspace_bytes() bytes, 256-byte aligned:
- *               it holds the rebuilt keys (content part) and values,
+ *               it holds both weights transposed ([num_heads, 128, d_latent]),
+ *               the rebuilt keys (content part) and values,
  *               [batch, num_heads, max_seq_len, 128] bf16 each, for every row
  *               below max_seq_len (the naive form rebuilds them all), then the
  *               split partials.

@@ -226,15 +226,15 @@ static void explicit_mla() {
           const int64_t cache_len = S > 0 ? S : 1;
           const kvattn_status st =
               kvattn_mla_explicit_decode(P, P, P, P, PI, P, nullptr, B, h, 512, 64, 128, 128, cache_len, S, 0.07f,
-                                         KVATTN_BF16, split, ws ? base : nullptr, ws, nullptr);
+                                         KVATTN_BF16, split, base, ws, nullptr);
           CHECK(st == KVATTN_OK, "B=%d h=%d S=%d split=%d: %s", B, h, S, split, kvattn_last_error());
           if (st != KVATTN_OK) continue;
-          if (ws > 0)
-            CHECK(kvattn_mla_explicit_decode(P, P, P, P, PI, P, nullptr, B, h, 512, 64, 128, 128, cache_len, S, 0.07f,
-                                             KVATTN_BF16, split, base, ws - 1, nullptr) == KVATTN_ERR_WORKSPACE,
-                  "short explicit workspace");
+          CHECK(kvattn_mla_explicit_decode(P, P, P, P, PI, P, nullptr, B, h, 512, 64, 128, 128, cache_len, S, 0.07f,
+                                           KVATTN_BF16, split, base, ws - 1, nullptr) == KVATTN_ERR_WORKSPACE,
+                "short explicit workspace");
           const kvattn::DecodeArgs& a = stub::last.args;
           const int64_t rec = (int64_t)B * h * S * 128 * 2;
+          const int64_t wbytes = (int64_t)h * 512 * 128 * 2;
           auto inside = [&](const void* p, int64_t bytes) {
             const unsigned char* c = static_cast<const unsigned char*>(p);
             return bytes == 0 || (c >= base && c + bytes <= base + ws);
@@ -248,11 +248,18 @@ static void explicit_mla() {
           }
           CHECK((int64_t)a.n_split * a.split_tokens >= S, "splits do not cover the sequence");
           CHECK(stub::last.n_projects == (S > 0 ? 2 : 0), "projections %d", stub::last.n_projects);
+          CHECK(stub::last.n_transposes == (S > 0 ? 2 : 0), "transposes %d", stub::last.n_transposes);
           if (S > 0) {
             const kvattn::ProjectArgs& pk = stub::last.projects[0];
             CHECK(pk.outer == B && pk.heads == h && pk.rows == S && pk.k_dim == 512 && pk.n_dim == 128, "shape");
             CHECK(pk.x_row == 576 && pk.x_head == 0 && pk.x_outer == cache_len * 576, "x strides");
-            CHECK(pk.w_head == 512 * 128 && !pk.w_transposed, "w stride");
+            CHECK(pk.w_head == 512 * 128 && pk.w_transposed, "w stride");
+            for (int tt = 0; tt < 2; ++tt) {
+              const auto& tr = stub::last.transposes[tt];
+              CHECK(tr.heads == h && tr.rows == 512 && tr.cols == 128 && inside(tr.dst, wbytes), "transpose");
+              CHECK(reinterpret_cast<const void*>(stub::last.projects[tt].w) == tr.dst, "projection reads other weights");
+            }
+            CHECK(stub::last.transposes[0].dst != stub::last.transposes[1].dst, "weights share a region");
             CHECK(pk.y_row == 128 && pk.y_head == (int64_t)S * 128 && pk.y_outer == (int64_t)h * S * 128, "y strides");
             CHECK(reinterpret_cast<const void*>(pk.y) == a.k && reinterpret_cast<const void*>(stub::last.projects[1].y) == a.v,
                   "attention reads other rows than the projections wrote");

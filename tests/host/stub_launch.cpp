@@ -41,6 +41,12 @@ hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t) {
 hipError_t launch_mla_explicit_attend(const DecodeArgs& a, hipStream_t, const LaunchEvents&) {
   return record("mla_explicit_attend", a);
 }
+hipError_t launch_transpose_heads(const void* src, void* dst, int heads, int rows, int cols, hipStream_t) {
+  stub::last.transposes[stub::last.n_transposes % 2] = {src, dst, heads, rows, cols};
+  ++stub::last.n_transposes;
+  ++stub::last.launches;
+  return hipSuccess;
+}
 hipError_t launch_merge(const DecodeArgs&, bool, hipStream_t) {
   ++stub::last.launches;
   ++stub::last.merges;

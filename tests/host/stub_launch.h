@@ -10,6 +10,12 @@ struct Record {
   kvattn::MlaPlanArgs plan{};
   kvattn::ProjectArgs projects[2]{};
   int n_projects = 0;
+  struct Transpose {
+    const void* src;
+    void* dst;
+    int heads, rows, cols;
+  } transposes[2]{};
+  int n_transposes = 0;
   int launches = 0;
   int merges = 0;
 };
