@@ -402,8 +402,15 @@ def sweep(torch, stream, names, steps, warmup, headline_name, headline_rates):
         w = W.WORKLOADS[name]
         print(f"[bench] sweep: {name}", file=sys.stderr, flush=True)
         prep = Prepared(w, 0, stream)
-        for i in range(warmup):
+        # Warm up for at least `warmup` calls and 200 ms, so that short calls run at the clocks
+        # long ones reach.
+        t_end = time.perf_counter() + 0.2
+        i = 0
+        while i < warmup or time.perf_counter() < t_end:
             prep.step(i)
+            i += 1
+            if i % 16 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         _, call_ms, kern_ms = timed_events(torch, prep, steps)
         out[name] = dict(rates(prep, call_ms, kern_ms), batch=w.batch, rotated_input_copies=prep.copies)
@@ -594,10 +601,6 @@ def main():
         roofline["mfma_tflops"] = head["mfma_tflops"]
         roofline["mfma_frac_of_bf16_peak"] = head["mfma_frac_of_bf16_peak"]
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU reference", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, prep.x0, args.cpu_seconds)
 
     cfg = {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "dtype": w.dtype,
            "rotated_input_copies": prep.copies, "split_tokens": args.split_tokens or "auto"}
@@ -611,10 +614,13 @@ def main():
     all_configs = None
     if not args.no_all_configs:
         head_rates = dict(head, batch=w.batch, rotated_input_copies=prep.copies)
-        del prep
-        torch.cuda.empty_cache()
         all_configs = sweep(torch, stream, SWEEP, args.sweep_steps, 10, w.name, head_rates)
         all_configs["mla_absorbed_vs_explicit"] = mla_forms(torch, stream, args.sweep_steps)
+    # The CPU reference last: the GPU idles meanwhile.
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU reference", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, prep.x0, args.cpu_seconds)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
