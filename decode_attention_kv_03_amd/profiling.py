@@ -14,7 +14,7 @@ device copy of known size, and records the hash of the kernel sources the
 counters were taken with.  ``bench.py`` reports that traffic only while the
 sources still hash the same.  ``mfma`` turns one ``--pmc MfmaUtil
 MfmaFlopsBF16 GRBM_GUI_ACTIVE`` run into the split-K kernel's counted
-matrix-core FLOPs, busy fraction and effective clock, with the kernel's mean
+matrix-core FLOPs, busy fraction and GRBM_GUI_ACTIVE rate, with the kernel's mean
 duration taken from its kernel-trace summary.  ``lds`` turns one ``--pmc
 SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_INSTS_LDS
 GRBM_GUI_ACTIVE`` run into the split-K kernel's LDS bank-conflict stall
@@ -149,8 +149,6 @@ def summarize_traffic(workload, out_md, fetch_dir, write_dir, copy_fetch_dir, co
                 f"write_bytes={write_b:.0f} -->\n")
 
 
-# Matrix-core rate of one MI355X compute unit at bf16: 4 SIMDs x 1024 FLOP per clock.
-BF16_FLOP_PER_CLK_PER_CU = 4096
 CUS = 256
 XCDS = 8
 BF16_PEAK_FLOPS = 2.5e15
@@ -181,11 +179,12 @@ def summarize_mfma(workload, out_md, run_dir, trace_md, algo_flops, command, ker
     gui, _ = _mean_counter(run_dir, "GRBM_GUI_ACTIVE", match)
     run_ns = _mean_dispatch_ns(run_dir, match)
     us = _trace_kernel_us(trace_md, match)
-    # GRBM_GUI_ACTIVE counts the clocks the GPU was busy during the dispatch, and the
-    # collection sums it over the XCDs (each has its own GRBM; the MfmaUtil expression
-    # takes their maximum instead), so one XCD's clocks are the sum / 8.
-    clk = gui / XCDS / (run_ns * 1e-9)
-    at_clock = algo_flops / (us * 1e-6) / (CUS * BF16_FLOP_PER_CLK_PER_CU * clk)
+    # GRBM_GUI_ACTIVE is summed over the XCDs (each has its own GRBM; the MfmaUtil
+    # expression takes their maximum instead), so one XCD's count is the sum / 8.  Its
+    # rate is the counter's own clock, not the shader clock: it reads above 2.4 GHz for
+    # the streaming kernels, while the shader clock measured inside the MLA kernel
+    # (s_memtime against s_memrealtime) is about 1.8 GHz.
+    rate = gui / XCDS / (run_ns * 1e-9)
     with open(out_md, "w") as f:
         what = f"`{kernel}`" if kernel else "the split-K kernel"
         f.write(f"# Matrix-core counters of {what}: {workload}\n\n")
@@ -199,11 +198,10 @@ def summarize_mfma(workload, out_md, run_dir, trace_md, algo_flops, command, ker
         f.write(f"| MfmaUtil (% of SIMD clocks with the matrix core busy) | {util:.1f} |\n")
         f.write(f"| GRBM_GUI_ACTIVE per dispatch (clocks, summed over the 8 XCDs) | {gui:.0f} |\n")
         f.write(f"| dispatch duration in the counter run (us) | {run_ns / 1e3:.2f} |\n")
-        f.write(f"| effective clock (GHz) | {clk / 1e9:.3f} |\n")
+        f.write(f"| GRBM_GUI_ACTIVE / 8 / dispatch duration (GHz; the counter's clock, not the shader clock) | {rate / 1e9:.3f} |\n")
         f.write(f"| kernel mean duration, kernel-trace run (us) | {us:.2f} |\n")
         f.write(f"| algorithmic FLOP rate (TFLOP/s) | {algo_flops / (us * 1e-6) / 1e12:.1f} |\n")
         f.write(f"| of the 2.5 PFLOP/s bf16 peak | {algo_flops / (us * 1e-6) / BF16_PEAK_FLOPS:.4f} |\n")
-        f.write(f"| of 256 CUs x 4096 FLOP/clock at the effective clock | {at_clock:.4f} |\n")
 
 
 def summarize_lds(workload, out_md, run_dir, command):
