@@ -39,6 +39,8 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn achieved HBM GB/s (% peak) + MFMA util (MLA); seq-steps/s per layer"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+CUS = 256
+BF16_FLOP_PER_CLK_PER_CU = 4096  # 4 SIMDs x 1024 bf16 FLOP per clock
 DEFAULT_WORKLOAD = "paged_gqa_h64_g8_b128_bs16_len1_32768"
 ROTATE_BYTES = 1 << 30  # rotate input copies until at least this many distinct bytes are cycled
 
@@ -321,6 +323,7 @@ class Prepared:
 def timed_events(torch, prep, steps, wall=False):
     """Time `steps` calls: (wall seconds of back-to-back calls or None, per-call ms, per-split-kernel ms).
 
+    Returns also, for MLA, the median shader clock (GHz) the split kernel's own stamps saw in region 3.
     Region 1 (only with `wall`): the calls back to back, wall time between two synchronisations,
     nothing else on the stream.  Region 2: HIP events around each whole call on the stream the
     kernels run on.  Region 3: HIP events around each call's split-K kernel alone
@@ -329,7 +332,7 @@ def timed_events(torch, prep, steps, wall=False):
     """
     import numpy as np
 
-    from decode_attention_kv_03_amd import time_next_kernel
+    from decode_attention_kv_03_amd import clock_next_mla, shader_clock_ghz, time_next_kernel
 
     stream = prep.stream
 
@@ -353,17 +356,27 @@ def timed_events(torch, prep, steps, wall=False):
         prep.step(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
+    # MLA: the same calls also stamp the shader clock inside their split kernel
+    # (kvattn_clock_next_mla), so the clock belongs to the kernel times reported.
+    stamps = None if prep.is_gqa else torch.zeros(steps, 4, dtype=torch.int64, device="cuda:0")
     for i in range(steps):
         time_next_kernel(kstarts[i], kends[i])
+        if stamps is not None:
+            clock_next_mla(stamps[i])
         prep.step(i)
     torch.cuda.synchronize()
     call_ms = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
     kern_ms = np.array([a.elapsed_time(b) for a, b in zip(kstarts, kends)])
-    return wall_s, call_ms, kern_ms
+    clock_ghz = None
+    if stamps is not None:
+        host = stamps.cpu()
+        clock_ghz = float(np.median([shader_clock_ghz(host[i]) for i in range(steps)]))
+    return wall_s, call_ms, kern_ms, clock_ghz
 
 
-def rates(prep, call_ms, kern_ms):
-    """Kernel and whole-call figures of one workload from its per-call and per-kernel times."""
+def rates(prep, call_ms, kern_ms, clock_ghz=None):
+    """Kernel and whole-call figures of one workload from its per-call and per-kernel times (and, for MLA,
+    the shader clock measured inside its kernel)."""
     import numpy as np
 
     w = prep.w
@@ -387,6 +400,11 @@ def rates(prep, call_ms, kern_ms):
         r["mfma_tflops"] = round(prep.flops / kern_s / 1e12, 1)
         r["mfma_frac_of_bf16_peak"] = round(prep.flops / kern_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
         r["call_mfma_frac_of_bf16_peak"] = round(prep.flops / call_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+        if clock_ghz:
+            # The bf16 peak at the clock the kernel actually ran at: 256 CUs x 4096 FLOP per clock.
+            peak_at_clock = CUS * BF16_FLOP_PER_CLK_PER_CU * clock_ghz * 1e9
+            r["shader_clock_ghz_in_kernel"] = round(clock_ghz, 3)
+            r["mfma_frac_at_measured_clock"] = round(prep.flops / kern_s / peak_at_clock, 4)
     return r
 
 
@@ -412,8 +430,8 @@ def sweep(torch, stream, names, steps, warmup, headline_name, headline_rates):
             if i % 16 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
-        _, call_ms, kern_ms = timed_events(torch, prep, steps)
-        out[name] = dict(rates(prep, call_ms, kern_ms), batch=w.batch, rotated_input_copies=prep.copies)
+        _, call_ms, kern_ms, clk = timed_events(torch, prep, steps)
+        out[name] = dict(rates(prep, call_ms, kern_ms, clk), batch=w.batch, rotated_input_copies=prep.copies)
         del prep
         torch.cuda.empty_cache()
     return out
@@ -562,10 +580,10 @@ def main():
         prep.step(i)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps}", file=sys.stderr, flush=True)
-    wall, call_ms, kern_ms = timed_events(torch, prep, args.steps, wall=True)
+    wall, call_ms, kern_ms, clock_ghz = timed_events(torch, prep, args.steps, wall=True)
     ms_per_step = wall * 1e3 / args.steps
     value = w.batch / (ms_per_step * 1e-3)
-    head = rates(prep, call_ms, kern_ms)
+    head = rates(prep, call_ms, kern_ms, clock_ghz)
 
     # Roofline of the dominant kernel (the split-K kernel that streams the cache): the call's
     # algorithmic bytes over its mean duration.  The whole call (plus the merge, and for MLA the plan)
@@ -600,6 +618,8 @@ def main():
     if not prep.is_gqa:
         roofline["mfma_tflops"] = head["mfma_tflops"]
         roofline["mfma_frac_of_bf16_peak"] = head["mfma_frac_of_bf16_peak"]
+        roofline["shader_clock_ghz_in_kernel"] = head.get("shader_clock_ghz_in_kernel")
+        roofline["mfma_frac_at_measured_clock"] = head.get("mfma_frac_at_measured_clock")
 
 
     cfg = {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "dtype": w.dtype,

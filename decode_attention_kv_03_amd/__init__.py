@@ -40,4 +40,6 @@ from .kvattn import (  # noqa: F401
     mla_up_project,
     mla_workspace_bytes,
     time_next_kernel,
+    clock_next_mla,
+    shader_clock_ghz,
 )

@@ -30,6 +30,14 @@ kvattn::LaunchEvents take_timing_events() {
   return ev;
 }
 
+thread_local uint64_t* g_clock_next = nullptr;
+
+uint64_t* take_clock_stamps() {
+  uint64_t* const p = g_clock_next;
+  g_clock_next = nullptr;
+  return p;
+}
+
 kvattn_status fail(kvattn_status s, const char* fmt, long long a = 0, long long b = 0) {
   char buf[256];
   std::snprintf(buf, sizeof(buf), fmt, a, b);
@@ -449,6 +457,7 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
                                 int32_t max_seq_len, float scale, kvattn_dtype dtype, int32_t split_tokens,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   const kvattn::LaunchEvents ev = take_timing_events();  // armed for this call only, whatever its outcome
+  uint64_t* const clock_stamps = take_clock_stamps();     // likewise
   kvattn_status st = check_mla(q, cache, seq_lens, out, batch, num_heads, d_latent, d_rope, dtype, scale);
   if (st != KVATTN_OK) return st;
   const bool paged = block_table != nullptr;
@@ -501,6 +510,7 @@ kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t*
   a.seq_pieces = pa.seq_pieces;
   a.plan_count = pa.plan_count;
   a.max_pieces = (int32_t)max_pieces;
+  a.clock_stamps = clock_stamps;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = kvattn::launch_mla_plan(pa, s);
   if (e != hipSuccess) return hip_status(e, "MLA plan kernel launch");
@@ -630,6 +640,12 @@ kvattn_status kvattn_time_next_kernel(void* start_event, void* stop_event) {
     return fail(KVATTN_ERR_INVALID, "start_event and stop_event must both be set or both be null");
   g_time_next.start = static_cast<hipEvent_t>(start_event);
   g_time_next.stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
+}
+
+kvattn_status kvattn_clock_next_mla(uint64_t* stamps) {
+  if (reinterpret_cast<uintptr_t>(stamps) % 8 != 0) return fail(KVATTN_ERR_INVALID, "stamps must be 8-byte aligned");
+  g_clock_next = stamps;
   return ok();
 }
 

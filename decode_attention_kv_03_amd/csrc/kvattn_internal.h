@@ -62,6 +62,10 @@ struct DecodeArgs {
   // whose columns 512.. hold the shared RoPE key.
   const void* rope;
   int32_t rec_len;
+  // Measurement only (MLA): when non-null, the first wave of workgroup 0
+  // stores {s_memtime, s_memrealtime} at the start and at the end of its tile
+  // loop here (four uint64 values).
+  uint64_t* clock_stamps;
 };
 
 // One batched per-head projection: for outer index o, head i and row m,

@@ -217,6 +217,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
+  // Measurement hook (off unless armed): the first wave of workgroup 0
+  // stamps the shader clock and real-time counters around its tile loop.
+  const bool stamp = a.clock_stamps != nullptr && blockIdx.x == 0 && wave == 0 && n_tiles > 0;
+  uint64_t clk0 = 0, rt0 = 0;
+  if (stamp) {
+    clk0 = __builtin_amdgcn_s_memtime();
+    rt0 = __builtin_amdgcn_s_memrealtime();
+  }
+
   f32x4 acc[kColBlocks][2];
 #pragma unroll
   for (int i = 0; i < kColBlocks; ++i)
@@ -451,6 +460,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
     if (n_tiles > 1) iteration(n_tiles - 1, TagFalse{}, TagTrue{});
     if (n_tiles > 1 && __builtin_expect(__any(need), 0)) rescale(alpha);
     values(n_tiles - 1, pp, []() {});
+  }
+
+  if (stamp) {
+    const uint64_t clk1 = __builtin_amdgcn_s_memtime();
+    const uint64_t rt1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) {
+      a.clock_stamps[0] = clk0;
+      a.clock_stamps[1] = rt0;
+      a.clock_stamps[2] = clk1;
+      a.clock_stamps[3] = rt1;
+    }
   }
 
   // Lane l holds O^T[col = 16*cb + 4*(l/16) + i][head 32*wave + 16*hb + l%16].

@@ -63,6 +63,7 @@ SIGNATURES = {
     "kvattn_gqa_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_mla_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "kvattn_time_next_kernel": (_c_i32, [_c_vp, _c_vp]),
+    "kvattn_clock_next_mla": (_c_i32, [_c_vp]),
     "kvattn_hbm_read_probe": (_c_i32, [_c_vp, _c_sz, _c_vp, _c_i32, _c_vp]),
     "kvattn_status_string": (ctypes.c_char_p, [_c_i32]),
     "kvattn_last_error": (ctypes.c_char_p, []),
@@ -161,6 +162,25 @@ def time_next_kernel(start_event, stop_event):
             raise ValueError("time_next_kernel: record each event once first so that it exists")
         handles.append(ctypes.c_void_p(h))
     _check(lib.kvattn_time_next_kernel(*handles))
+
+
+def clock_next_mla(stamps):
+    """Arm the next mla_decode call on this thread to store {shader clock, 100 MHz real-time} counter pairs
+    at the start and end of its split kernel's tile loop into ``stamps`` (a CUDA int64 tensor of at least 4
+    elements; measurement utility, see kvattn_clock_next_mla).  None disarms."""
+    lib = load_library()
+    if stamps is None:
+        _check(lib.kvattn_clock_next_mla(None))
+        return
+    if not stamps.is_cuda or stamps.dtype != torch.int64 or stamps.numel() < 4 or not stamps.is_contiguous():
+        raise ValueError("clock_next_mla: stamps must be a contiguous CUDA int64 tensor of at least 4 elements")
+    _check(lib.kvattn_clock_next_mla(ctypes.c_void_p(stamps.data_ptr())))
+
+
+def shader_clock_ghz(stamps):
+    """Shader clock in GHz from the four values clock_next_mla had stored."""
+    v = [int(t) for t in stamps[:4].tolist()]
+    return (v[2] - v[0]) / ((v[3] - v[1]) * 10.0)
 
 
 def gqa_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size=0, split_tokens=0,

@@ -32,6 +32,20 @@ extern "C" {
 kvattn_status kvattn_time_next_kernel(void* start_event, void* stop_event);
 
 /*
+ * Measurement utility: the next kvattn_mla_decode call made on the calling
+ * thread has the first wave of its split kernel's workgroup 0 store four
+ * uint64 values at `stamps` (device memory, 8-byte aligned, owned by the
+ * caller): the shader clock counter (s_memtime) and the 100 MHz real-time
+ * counter (s_memrealtime) when its tile loop starts, then both again when
+ * it ends.  The ratio of the two differences is the shader clock the kernel
+ * ran at, from which a matrix-core peak at the measured clock follows.
+ * NULL disarms.  Consumed by that next call whether or not it succeeds;
+ * nothing is stored if the call fails before its launch or its workgroup 0
+ * has no tokens.
+ */
+kvattn_status kvattn_clock_next_mla(uint64_t* stamps);
+
+/*
  * Measurement utility, not part of the attention path: stream `bytes` bytes
  * of device memory at `buf` through 16-byte loads with `workgroups`
  * workgroups of 256 threads, to measure the device's practical HBM read

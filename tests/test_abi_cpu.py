@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     assert "kvattn_gqa_decode" in names and "kvattn_mla_decode" in names
     # the attention header holds the operations, sizing queries and error calls only
     assert not set(names) & set(measure)
-    assert measure == ["kvattn_hbm_read_probe", "kvattn_time_next_kernel"]
+    assert measure == ["kvattn_clock_next_mla", "kvattn_hbm_read_probe", "kvattn_time_next_kernel"]
     for n in names + measure:
         assert hasattr(lib, n), n
     assert sorted(K.SIGNATURES) == sorted(names + measure)
@@ -202,6 +202,19 @@ def test_time_next_kernel_arms_both_events_or_none():
     st = lib.kvattn_gqa_decode(None, None, None, None, None, None, None, 1, 8, 2, 128, 16, 0, 0, 16, 0.1,
                                K.KVATTN_BF16, 0, None, 0, None)
     assert st == K.KVATTN_ERR_INVALID
+
+
+def test_clock_hook_checks_alignment_and_python_side_tensor():
+    """The MLA clock hook stores a device pointer only; a misaligned one is rejected, and the binding
+    refuses tensors that are not contiguous CUDA int64 of at least 4 elements."""
+    import torch
+
+    assert lib.kvattn_clock_next_mla(ctypes.c_void_p(0x1004)) == K.KVATTN_ERR_INVALID
+    assert lib.kvattn_clock_next_mla(ctypes.c_void_p(0x1000)) == K.KVATTN_OK
+    assert lib.kvattn_clock_next_mla(None) == K.KVATTN_OK
+    with pytest.raises(ValueError):
+        K.clock_next_mla(torch.zeros(4, dtype=torch.int64))
+    assert K.shader_clock_ghz(torch.tensor([100, 10, 2100, 110])) == pytest.approx(2.0)
 
 
 def test_noalloc_rejects_calls_beyond_its_scratch_before_touching_the_gpu():

@@ -170,3 +170,24 @@ def test_paged_full_size_sampled():
     assert torch.isfinite(out.float()).all()
     del x
     torch.cuda.empty_cache()
+
+
+def test_clock_stamps_hook():
+    """kvattn_clock_next_mla: the armed call stores sane counter stamps and computes the same output."""
+    from decode_attention_kv_03_amd import clock_next_mla, shader_clock_ghz
+
+    w = W.shrink(W.WORKLOADS["deepseek_v2_mla_h128_b32_s8192"], batch=8, seq_len=4000)
+    note("mla clock stamps")
+    x = W.make_mla_inputs(w, DEV)
+    plain, plain_lse = run(x)
+    stamps = torch.zeros(4, dtype=torch.int64, device=DEV)
+    clock_next_mla(stamps)
+    armed, armed_lse = run(x)
+    assert torch.equal(plain, armed) and torch.equal(plain_lse, armed_lse)
+    v = stamps.cpu().tolist()
+    assert v[2] > v[0] > 0 and v[3] > v[1] > 0, v
+    assert 0.3 < shader_clock_ghz(stamps.cpu()) < 3.0
+    # Consumed by that call: the next one leaves a fresh buffer untouched.
+    fresh = torch.zeros(4, dtype=torch.int64, device=DEV)
+    run(x)
+    assert int(fresh.abs().sum()) == 0
