@@ -208,8 +208,8 @@ def hbm_probe(torch, stream, nbytes=2 << 30, copies=1, workgroups=(1024, 2048, 4
     cycle through that many separate buffers, as the timed decode calls cycle through their input
     copies, so a launch of a smaller size finds nothing in the last-level cache either.  For each
     workgroup count the launch reads the largest multiple of 16 KiB per workgroup that fits in
-    `nbytes` (the probe splits its buffer evenly in 16 KiB tiles; an uneven rest would be read by a
-    single workgroup), and the rate is taken over the bytes actually read.
+    `nbytes` (the probe splits its buffer evenly in 16 KiB tiles and reads an uneven rest with plain
+    loads), and the rate is taken over the bytes actually read.
     """
     from decode_attention_kv_03_amd import hbm_read_probe
 

@@ -374,9 +374,105 @@ __global__ __launch_bounds__(256) void mla_explicit_attend(DecodeArgs a) {
   }
 }
 
+
+// Few-row projection with a [K, N] weight (rows <= 32: the decode batch, as
+// in the absorbed layer's W_uv up-projection).  There the 128-row tiles above
+// would compute mostly padding, and each workgroup's K loop waits on one
+// load after another.  Here one workgroup owns (outer, head, 32 output
+// columns) for all rows.  Every load it needs is issued before the first is
+// used (one memory latency): the rows of x straight into the B fragments of
+// v_mfma_f32_16x16x32_bf16 (contiguous along k), and the [kK, 32] weight
+// slice through registers into LDS (rows padded by 16 bytes), from where the
+// transposing reads deliver the A fragments.  Wave w computes the block
+// Y^T[16 columns x 16 rows] = W^T X^T of column block w/2 and row block w%2;
+// rows past `rows` are loaded as zeros and never stored.  A [N, K] weight
+// (query absorption) has no such path: the tiled kernel above already runs
+// it at the speed of a plain read of its bytes.
+constexpr int kFewRows = 32;
+constexpr int kFewNt = 32;                    // output columns per workgroup
+constexpr int kFewWPitch = kFewNt * 2 + 16;   // bytes per staged weight row
+
+template <int kK>
+__global__ __launch_bounds__(256) void latent_project_few(ProjectArgs p) {
+  constexpr int kSteps = kK / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char wst[kK * kFewWPitch];
+  const int n_slices = p.n_dim / kFewNt;
+  const int slice = blockIdx.x % n_slices;
+  const int oi = blockIdx.x / n_slices;  // outer * heads + head
+  const int head = oi % p.heads, o = oi / p.heads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+  const int nb = wave >> 1, rb = wave & 1;
+  const uint16_t* xg = p.x + (int64_t)o * p.x_outer + (int64_t)head * p.x_head;
+  const uint16_t* wg = p.w + (int64_t)head * p.w_head + (int64_t)slice * kFewNt;
+
+  // B operand X^T: lane l holds x row 16*rb + l%16 at k 32*ks + 8*(l/16) .. +7.
+  const int row = 16 * rb + n16;
+  bf16x8 xf[kSteps];
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < p.rows) v = *reinterpret_cast<const u32x4*>(xg + (int64_t)row * p.x_row + 32 * ks + 8 * g);
+    xf[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+  // The weight slice: thread t moves 16-byte pieces t, t+256, ... (row piece/4, chunk piece%4).
+  constexpr int kPer = kK * (kFewNt / 8) / 256;
+  static_assert(kK * (kFewNt / 8) % 256 == 0, "whole pieces per thread");
+  u32x4 wv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = tid + 256 * u;
+    wv[u] = *reinterpret_cast<const u32x4*>(wg + (int64_t)(c >> 2) * p.n_dim + 8 * (c & 3));
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = tid + 256 * u;
+    *reinterpret_cast<u32x4*>(wst + (c >> 2) * kFewWPitch + 16 * (c & 3)) = wv[u];
+  }
+  __syncthreads();
+
+  // A operand W^T: lane n of a 16-lane group addresses row 32*ks + 8*g + n/4
+  // (and +4) at columns 16*nb + 4*(n%4) .. +3, and receives column 16*nb + n.
+  const auto* wl = (const __attribute__((address_space(3))) unsigned char*)wst;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    const int off = (32 * ks + 8 * g + (n16 >> 2)) * kFewWPitch + (16 * nb + 4 * (n16 & 3)) * 2;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(wl + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(wl + off + 4 * kFewWPitch));
+    const bf16x8 aop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, xf[ks], acc, 0, 0, 0);
+  }
+  // Lane l holds Y^T[column 16*nb + 4*(l/16) + v][row 16*rb + l%16].
+  if (row < p.rows) {
+    uint16_t* y = p.y + (int64_t)o * p.y_outer + (int64_t)head * p.y_head + (int64_t)row * p.y_row +
+                  slice * kFewNt + 16 * nb + 4 * g;
+    *reinterpret_cast<uint2*>(y) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+  }
+}
+
+// The few-row path applies to [K, N] weights, rows <= 32 and the reduction
+// lengths it is compiled for; it returns false (and launches nothing)
+// otherwise.
+bool launch_few(const ProjectArgs& p, hipStream_t stream, hipError_t& err) {
+  if (p.w_transposed || p.rows > kFewRows || p.n_dim % kFewNt != 0) return false;
+  const int64_t blocks = (int64_t)p.outer * p.heads * (p.n_dim / kFewNt);
+  if (blocks <= 0 || blocks > 0x7fffffff) return false;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (p.k_dim == 512) latent_project_few<512><<<grid, block, 0, stream>>>(p);
+  else if (p.k_dim == 128) latent_project_few<128><<<grid, block, 0, stream>>>(p);
+  else if (p.k_dim == 64) latent_project_few<64><<<grid, block, 0, stream>>>(p);
+  else return false;
+  err = hipGetLastError();
+  return true;
+}
+
 }  // namespace
 
 hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream) {
+  hipError_t few_err = hipSuccess;
+  if (launch_few(p, stream, few_err)) return few_err;
   const int64_t blocks = (int64_t)p.outer * p.heads * p.m_tiles * p.n_tiles;
   if (blocks <= 0 || blocks > 0x7fffffff || p.k_dim % kBK != 0 || p.n_dim % kBN != 0) return hipErrorInvalidValue;
   if (p.w_transposed) latent_project<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);

@@ -9,7 +9,8 @@ namespace {
 // Each workgroup streams one contiguous chunk of the buffer: per 16 KiB
 // tile, its four waves issue 16-byte global -> LDS copies (non-temporal),
 // three tiles in flight, and read one word of each tile back so the copies
-// are observable.  The last partial tile is read with plain loads.
+// are observable.  What the whole tiles leave over is read with plain loads
+// by the whole grid.
 __global__ __launch_bounds__(256) void hbm_read(const unsigned char* __restrict__ p, int64_t bytes, uint32_t* sink) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4][16384];
   const int64_t per = (bytes / gridDim.x) & ~int64_t(16383);
@@ -37,11 +38,13 @@ __global__ __launch_bounds__(256) void hbm_read(const unsigned char* __restrict_
     if (t + 3 < ntiles) issue(t + 3);
     acc ^= *reinterpret_cast<const uint32_t*>(&lds[t & 3][tid * 4]);
   }
-  // Whatever the even split left over at the end of the buffer.
+  // Whatever the even split left over at the end of the buffer (all of it
+  // when the buffer holds less than one tile per workgroup), spread over the
+  // whole grid.
   const int64_t rest = bytes - per * gridDim.x;
-  if (blockIdx.x == gridDim.x - 1)
-    for (int64_t i = (int64_t)tid * 16; i < rest; i += 256 * 16)
-      acc ^= *reinterpret_cast<const uint32_t*>(p + per * gridDim.x + i);
+  const unsigned char* tail = p + per * gridDim.x;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + tid) * 16; i < rest; i += (int64_t)gridDim.x * 256 * 16)
+    acc ^= *reinterpret_cast<const uint32_t*>(tail + i);
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 

@@ -278,3 +278,23 @@ def test_out_of_range_table_entries_stay_contained(kind, bs):
         o = out.float()
         assert torch.isfinite(o).all()
         assert_close(o[0:1].cpu().numpy(), ref, "untouched sequence", f32=kind == "f32")
+
+
+def test_read_probe_handles_buffers_smaller_than_its_grid():
+    """The streaming-read probe reads what its whole tiles leave over with the whole grid: a buffer of
+    less than one 16 KiB tile per workgroup finishes as fast as a tiled one."""
+    import time
+
+    from decode_attention_kv_03_amd import hbm_read_probe
+
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for nbytes, wgs in ((1 << 20, 4096), (48 * 1024 + 16, 8), (64 * 16384, 64)):
+        note(f"read probe {nbytes} bytes, {wgs} workgroups")
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+        hbm_read_probe(buf, wgs, sink)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            hbm_read_probe(buf, wgs, sink)
+        torch.cuda.synchronize()
+        assert (time.perf_counter() - t0) / 10 < 0.05

@@ -54,7 +54,7 @@ def f64(t):
     return oracle.bf16_bits_to_f64(W.host_view(t))
 
 
-@pytest.mark.parametrize("B,h,d_v", [(5, 16, 128), (300, 8, 256), (32, 128, 128), (1, 1, 128)])
+@pytest.mark.parametrize("B,h,d_v", [(5, 16, 128), (300, 8, 256), (32, 128, 128), (1, 1, 128), (17, 4, 256), (33, 4, 128)])
 def test_up_projection_matches_oracle(B, h, d_v):
     gen = torch.Generator(DEV).manual_seed(B + h)
     o_lat = torch.randn((B, h, 512), generator=gen, device=DEV).to(torch.bfloat16)
@@ -68,7 +68,7 @@ def test_up_projection_matches_oracle(B, h, d_v):
     assert_close(out.tensor.float().cpu().numpy(), ref, "up-projection")
 
 
-@pytest.mark.parametrize("B,h", [(3, 16), (130, 4), (32, 128)])
+@pytest.mark.parametrize("B,h", [(3, 16), (130, 4), (32, 128), (16, 8), (33, 2)])
 def test_query_absorption_matches_oracle(B, h):
     gen = torch.Generator(DEV).manual_seed(7 * B + h)
     q_c = torch.randn((B, h, 128), generator=gen, device=DEV).to(torch.bfloat16)
@@ -85,6 +85,31 @@ def test_query_absorption_matches_oracle(B, h):
     qc64, wuk64 = f64(q_c), f64(w_uk)
     ref = np.stack([oracle.mla_absorb_query(qc64[b], wuk64) for b in range(B)])
     assert_close(q_abs.tensor[..., :512].float().cpu().numpy(), ref, "absorption")
+
+
+@pytest.mark.parametrize("wt", [False, True])
+@pytest.mark.parametrize("outer,heads,rows,k,n", [(3, 2, 7, 64, 256), (2, 3, 32, 512, 128), (1, 5, 1, 128, 512),
+                                                  (2, 2, 40, 64, 128)])
+def test_projection_raw_strides(wt, outer, heads, rows, k, n):
+    """kvattn_mla_project with an outer dimension and interleaved rows, on both weight layouts: the few-row
+    path (rows <= 32) and the tiled one (rows 40) against the oracle's per-head product."""
+    from decode_attention_kv_03_amd import mla_project
+
+    gen = torch.Generator(DEV).manual_seed(outer * 1000 + heads * 100 + rows + k + n + int(wt))
+    x = torch.randn((outer, rows, heads, k), generator=gen, device=DEV).to(torch.bfloat16)
+    w = (torch.randn((heads, n, k) if wt else (heads, k, n), generator=gen, device=DEV) / k ** 0.5).to(torch.bfloat16)
+    note(f"projection outer={outer} heads={heads} rows={rows} k={k} n={n} transposed={wt}")
+    y = fenced((outer, rows, heads, n), torch.bfloat16)
+    mla_project(x, w, y.tensor, outer=outer, heads=heads, rows=rows, k_dim=k, n_dim=n,
+                x_strides=(rows * heads * k, k, heads * k), w_head_stride=n * k,
+                y_strides=(rows * heads * n, n, heads * n), w_transposed=wt)
+    torch.cuda.synchronize()
+    assert y.bands_intact()
+    w64 = f64(w)
+    if wt:
+        w64 = np.ascontiguousarray(np.transpose(w64, (0, 2, 1)))
+    ref = oracle.mla_up_project(f64(x).reshape(outer * rows, heads, k), w64).reshape(outer, rows, heads, n)
+    assert_close(y.tensor.float().cpu().numpy(), ref, "projection")
 
 
 def explicit_reference(x, rows=None):
