@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one full library call (split-K kernel plus, when the call splits,
-the log-sum-exp merge; for MLA also the work-plan kernel) over the
+the log-sum-exp merge; for MLA and for the persistent GQA form of paged
+batches also the device-side work-plan kernel) over the
 workload's synthetic inputs, already resident in HBM.  The default workload
 is the largest single-GPU configuration, the paged GQA layer (h=64, g=8,
 d=128, bf16, batch 128, 16-token blocks, lengths uniform on 1..32768).
@@ -606,8 +607,9 @@ def main():
         "intensity_flop_per_byte": head["intensity_flop_per_byte"],
         "traffic_detail": traffic,
         "call_us_mean": head["call_us_mean"],
-        "call_note": "whole library call: split-K kernel plus the log-sum-exp merge when the call splits "
-                     "(MLA: plus the work-plan kernel); call_frac is the target figure, frac the kernel's own",
+        "call_note": "whole library call: split-K kernel plus the log-sum-exp merge when the call splits, and "
+                     "the device-side work-plan kernel of MLA and of the persistent GQA form (paged or ragged "
+                     "batches with many splits); call_frac is the target figure, frac the kernel's own",
         "call_achieved_gbs": head["call_gbs"],
         "call_frac": head["call_frac"],
         "measured_read_ceiling_gbs": probe["gbs"],

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvattn.so")
-SOURCES = ["api.cpp", "gqa_f32.hip", "gqa_bf16.hip", "gqa_fp8.hip", "mla_bf16.hip", "mla_plan.hip", "merge.hip", "probe.hip", "noalloc.hip", "mla_explicit.hip"]
+SOURCES = ["api.cpp", "gqa_f32.hip", "gqa_bf16.hip", "gqa_fp8.hip", "gqa_plan.hip", "mla_bf16.hip", "mla_plan.hip", "merge.hip", "probe.hip", "noalloc.hip", "mla_explicit.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

@@ -163,6 +163,30 @@ struct GqaCache {
   CacheKind kind;
 };
 
+// Workspace of the persistent GQA form: the split partials (`partials`
+// bytes), then the work list (one int4 per possible item), then its count and
+// claim counter.  total = 0 when the call keeps one workgroup per split: an
+// fp32 cache, a single split, a grid that fits in about two rounds of
+// resident workgroups, or a paged layout whose full tiles need the LDS table
+// (block size not a power of two, or below one copy instruction's rows: 4
+// bf16 rows, 8 fp8 rows).
+struct GqaPersistentLayout {
+  size_t items, ctl, total;
+};
+
+GqaPersistentLayout gqa_persistent_layout(CacheKind kind, int64_t batch, int64_t g, int64_t nsplit, int32_t block_size,
+                                          size_t partials) {
+  GqaPersistentLayout l{0, 0, 0};
+  const int64_t slots = batch * g * nsplit;
+  const int32_t min_shift = kind == CacheKind::kFp8E4m3 ? 3 : 2;
+  if (kind == CacheKind::kF32 || nsplit <= 1 || slots <= 4 * kvattn::kPersistentWorkgroups) return l;
+  if (block_size > 0 && pow2_shift(block_size) < min_shift) return l;
+  l.items = (size_t)round_up((int64_t)partials, 256);
+  l.ctl = l.items + (size_t)round_up(slots * 16, 256);
+  l.total = l.ctl + 256;
+  return l;
+}
+
 // Geometry checks, split planning and launches shared by the GQA entry points
 // (their operand checks have already run).
 kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCache& cache,
@@ -198,7 +222,14 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   // Partial outputs are fp32 for an fp32 cache and bf16 otherwise (the
   // workspace query sizes the fp32 layout, which bounds both).
   const size_t part_elem = cache.kind == CacheKind::kF32 ? sizeof(float) : sizeof(uint16_t);
-  const size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim, (int64_t)part_elem);
+  size_t need = partial_bytes(batch, num_q_heads, nsplit, head_dim, (int64_t)part_elem);
+  // A grid of splits that would run in many rounds takes the persistent form
+  // instead, with its work list after the partials, when the workspace holds
+  // it (the bf16 partials leave room for it in the size the query reports).
+  const GqaPersistentLayout pl =
+      gqa_persistent_layout(cache.kind, batch, num_kv_heads, nsplit, paged ? block_size : 0, need);
+  const bool persistent = pl.total > 0 && pl.total <= wsrc.bytes && (wsrc.resolve != nullptr || wsrc.ptr != nullptr);
+  if (persistent) need = pl.total;
   void* workspace = wsrc.ptr;
   if (need > 0) {
     if (wsrc.resolve != nullptr) {
@@ -244,6 +275,23 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipErrorInvalidValue;
+  if (persistent) {
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    kvattn::GqaPlanArgs p{};
+    p.seq_lens = seq_lens;
+    p.batch = batch;
+    p.g = num_kv_heads;
+    p.len_cap = max_seq_len;
+    p.window = window;
+    p.split = split;
+    p.n_split = nsplit;
+    p.items = reinterpret_cast<int4*>(ws + pl.items);
+    p.ctl = reinterpret_cast<int32_t*>(ws + pl.ctl);
+    a.items = p.items;
+    a.items_ctl = p.ctl;
+    e = kvattn::launch_gqa_plan(p, s);
+    if (e != hipSuccess) return hip_status(e, "plan kernel launch");
+  }
   switch (cache.kind) {
     case CacheKind::kF32: e = kvattn::launch_gqa_f32(a, s, ev); break;
     case CacheKind::kBf16: e = kvattn::launch_gqa_bf16(a, s, ev); break;

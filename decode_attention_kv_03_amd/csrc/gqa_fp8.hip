@@ -151,25 +151,36 @@ __global__ __launch_bounds__(256, 2) void gqa_split_fp8(DecodeArgs a) {
   gqa_split_body<Fp8Format, GqaAttn16<Fp8Format, HBW, WH>>(a);
 }
 
+template <int HBW, int WH>
+__global__ __launch_bounds__(256, 2) void gqa_split_fp8_persistent(DecodeArgs a) {
+  gqa_persistent_body<Fp8Format, GqaAttn16<Fp8Format, HBW, WH>>(a);
+}
+
+// One workgroup per (sequence, KV head, split), or, with a work list, the
+// resident workgroups of the persistent form.
+template <int HBW, int WH>
+hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
+  const dim3 block(256);
+  if (a.items != nullptr) {
+    hipExtLaunchKernelGGL((gqa_split_fp8_persistent<HBW, WH>), dim3(kPersistentWorkgroups), block, 0, stream,
+                          ev.start, ev.stop, 0, a);
+  } else {
+    const int64_t units = (int64_t)a.batch * a.num_kv_heads;
+    const dim3 grid((unsigned)(8 * ((units + 7) / 8) * a.n_split));
+    hipExtLaunchKernelGGL((gqa_split_fp8<HBW, WH>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gqa_fp8(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev) {
-  const int64_t units = (int64_t)a.batch * a.num_kv_heads;
-  const dim3 grid((unsigned)(8 * ((units + 7) / 8) * a.n_split));
-  const dim3 block(256);
   const int head_blocks = (a.group + 15) / 16;
-  if (head_blocks == 1) {
-    hipExtLaunchKernelGGL((gqa_split_fp8<1, 4>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
-  } else if (head_blocks == 2) {
-    hipExtLaunchKernelGGL((gqa_split_fp8<1, 2>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
-  } else if (head_blocks <= 4) {
-    hipExtLaunchKernelGGL((gqa_split_fp8<1, 1>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
-  } else if (head_blocks <= 8) {
-    hipExtLaunchKernelGGL((gqa_split_fp8<2, 1>), grid, block, 0, stream, ev.start, ev.stop, 0, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (head_blocks == 1) return launch_shape<1, 4>(a, stream, ev);
+  if (head_blocks == 2) return launch_shape<1, 2>(a, stream, ev);
+  if (head_blocks <= 4) return launch_shape<1, 1>(a, stream, ev);
+  if (head_blocks <= 8) return launch_shape<2, 1>(a, stream, ev);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvattn

@@ -90,7 +90,8 @@ __device__ __forceinline__ bool gqa_work(const DecodeArgs& a, GqaWork& w) {
 // kRows*(i%16) + l/kChunks, chunk l%kChunks), which holds logical chunk
 // (l%kChunks) ^ swz(row).  Rows past the split's end re-read its last row
 // (masked out of the softmax); an out-of-range table entry reads an
-// in-bounds stand-in row.
+// in-bounds stand-in row.  Without an LDS table (tbl_lds null, the persistent
+// kernel) the general path reads the block table from global memory.
 template <class F>
 struct GqaCopier {
   static constexpr int kRows = 1024 / F::kRowB;
@@ -114,8 +115,7 @@ struct GqaCopier {
     vbase = static_cast<const unsigned char*>(a.v);
     paged = a.block_size != 0;
     bs = a.block_size;
-    table_row = paged ? a.block_table + (int64_t)w.b * a.max_blocks : nullptr;
-    head_rows = (int64_t)(w.b * a.num_kv_heads + w.j) * a.cache_len;
+    bind(w);
     win_first = 0;
     // Paged fast path: an instruction's rows start at a multiple of kRows
     // tokens and so lie in one block; the per-lane byte offset depends on
@@ -126,6 +126,14 @@ struct GqaCopier {
       const int row = kRows * u4 + lane / kChunks;
       dpo[u4] = (uint32_t)((lane / kChunks) * F::kRowB + ((lane % kChunks) ^ F::swz(row)) * 16);
     }
+  }
+
+  // Point the copies at another work item (the persistent kernel).
+  __device__ __forceinline__ void bind(const GqaWork& w) {
+    j = w.j;
+    t_end = w.t_end;
+    table_row = paged ? a.block_table + (int64_t)w.b * a.max_blocks : nullptr;
+    head_rows = (int64_t)(w.b * a.num_kv_heads + w.j) * a.cache_len;
   }
 
   __device__ __forceinline__ void load_window(int first) {
@@ -144,7 +152,7 @@ struct GqaCopier {
   }
 
   __device__ __forceinline__ void issue(int t0, uint32_t stage_base) {
-    if (paged && (min(t0 + F::kTile, t_end) - 1) / bs >= win_first + kGqaTblSlots) {
+    if (paged && tbl != nullptr && (min(t0 + F::kTile, t_end) - 1) / bs >= win_first + kGqaTblSlots) {
       // slide the table window (drains the copies in flight)
       __builtin_amdgcn_s_waitcnt(0x0070);
       __syncthreads();
@@ -182,24 +190,32 @@ struct GqaCopier {
       }
       return;
     }
+    // Table lookups first (all in flight together), then the source
+    // addresses, then the copies.
+    int tok[8], blk[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int row = kRows * ((wave * 8 + u) & 15) + lane / kChunks;
+      tok[u] = min(t0 + row, t_end - 1);
+      // The staged table window, or (no LDS table) the block table itself.
+      if (paged) blk[u] = tbl != nullptr ? tbl[tok[u] / bs - win_first] : table_row[tok[u] / bs];
+    }
+    // Global table entries: one visible wait for all of them here, so that
+    // no wait between the copies below drains the ones already issued.
+    if (paged && tbl == nullptr) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int inst = wave * 8 + u;
-      const int tensor = inst >> 4, rg = inst & 15;
-      const int row = kRows * rg + lane / kChunks;
+      const int row = kRows * (inst & 15) + lane / kChunks;
       const int chunk = (lane % kChunks) ^ F::swz(row);
-      const int t = min(t0 + row, t_end - 1);
-      int64_t row_index;
-      if (!paged) {
-        row_index = head_rows + t;
-      } else {
-        const int q = t / bs;
-        const int blk = tbl[q - win_first];
-        row_index = (blk >= 0 && (int64_t)blk < a.cache_len) ? ((int64_t)blk * a.num_kv_heads + j) * bs + (t - q * bs)
-                                                              : 0;  // out-of-range entry: an in-bounds stand-in row
+      int64_t row_index = head_rows + tok[u];
+      if (paged) {
+        const bool in_range = blk[u] >= 0 && (int64_t)blk[u] < a.cache_len;  // else an in-bounds stand-in row
+        const int64_t b64 = in_range ? blk[u] : 0;
+        row_index = in_range ? (b64 * a.num_kv_heads + j) * bs + tok[u] % bs : 0;
       }
-      const unsigned char* src = (tensor == 0 ? kbase : vbase) + row_index * F::kRowB + chunk * 16;
-      dma16(src, stage_base + tensor * kGqaTileBytes + rg * 1024);
+      const unsigned char* src = ((inst >> 4) == 0 ? kbase : vbase) + row_index * F::kRowB + chunk * 16;
+      dma16(src, stage_base + (inst >> 4) * kGqaTileBytes + (inst & 15) * 1024);
     }
   }
 };
@@ -287,26 +303,33 @@ struct GqaAttn16 {
     }
   }
 
-  // Merge the token-split waves (through the idle ring), then write the
-  // output or the split's partial.  Lane l holds O^T[d = 16*db + 4*grp + v][head n16].
-  __device__ __forceinline__ void finish(const DecodeArgs& a, const GqaWork& w, unsigned char* ring, int wave) {
+  // Merge the token-split waves through `red` (an idle 32 KiB ring stage),
+  // then write the output or the split's partial; the waves of a head block
+  // other than its first only hand over their state.  Lane l holds
+  // O^T[d = 16*db + 4*grp + v][head n16].
+  __device__ __forceinline__ void finish(const DecodeArgs& a, const GqaWork& w, unsigned char* red_stage, int wave) {
 #pragma unroll
     for (int hbi = 0; hbi < HBW; ++hbi) l_run[hbi] = sum_over_row_groups(l_run[hbi]);
     if constexpr (WH > 1) {
+      static_assert((4 / WH) * (WH - 1) * kGqaRedFloatsPerWave * 4 <= kGqaStageBytes, "merge state fits a stage");
+      // Slot of token slot t (1 .. WH-1) of this wave's head block.
+      const int slot0 = (wave / WH) * (WH - 1) - 1;
       __syncthreads();
-      float* red = reinterpret_cast<float*>(ring);
-      float* mine = red + wave * kGqaRedFloatsPerWave;
+      float* red = reinterpret_cast<float*>(red_stage);
+      if (ts != 0) {
+        float* mine = red + (slot0 + ts) * kGqaRedFloatsPerWave;
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mine[(db * 4 + v) * 64 + lane] = acc[0][db][v];
-      mine[32 * 64 + lane] = m_ref[0];
-      mine[33 * 64 + lane] = l_run[0];
+          for (int v = 0; v < 4; ++v) mine[(db * 4 + v) * 64 + lane] = acc[0][db][v];
+        mine[32 * 64 + lane] = m_ref[0];
+        mine[33 * 64 + lane] = l_run[0];
+      }
       __syncthreads();
       if (ts != 0) return;
 #pragma unroll
       for (int w2 = 1; w2 < WH; ++w2) {
-        const float* other = red + (wave + w2) * kGqaRedFloatsPerWave;
+        const float* other = red + (slot0 + w2) * kGqaRedFloatsPerWave;
         const float m2 = other[32 * 64 + lane];
         const float l2 = other[33 * 64 + lane];
         const float M = fmaxf(m_ref[0], m2);
@@ -381,6 +404,116 @@ __device__ __forceinline__ void gqa_split_body(const DecodeArgs& a) {
     attn.tile(ring[it & 1], w.t_begin + it * F::kTile, w.t_end, w.t_lo);
   }
   attn.finish(a, w, &ring[0][0], wave);
+}
+
+// The work of one item of the device-side list (gqa_plan.hip).  The
+// sliding window's first attended token is looked up only when `with_lo`.
+template <int kTile>
+__device__ __forceinline__ GqaWork gqa_item_work(const DecodeArgs& a, const int4& item, bool with_lo) {
+  GqaWork w;
+  w.b = item.x / a.num_kv_heads;
+  w.j = item.x - w.b * a.num_kv_heads;
+  w.split = item.y;
+  w.t_begin = item.z;
+  w.t_end = item.w;
+  w.t_lo = with_lo && a.window > 0 ? window_first(clamp_len(a.seq_lens[w.b], a.len_cap), a.window) : 0;
+  w.n_tiles = (w.t_end - w.t_begin + kTile - 1) / kTile;
+  w.final_out = false;
+  return w;
+}
+
+// Persistent form of the split kernel, for calls whose grid of splits would
+// run in many rounds (ragged or paged batches).  Two resident workgroups per
+// compute unit take the items of the device-side list one at a time from a
+// counter (a vector atomic, one per item), in list order; an item is computed
+// exactly as the grid-per-split body computes its split, so which workgroup
+// takes it does not change any result.  A workgroup claims its next item
+// three tiles before the current one ends (late enough that the items go to
+// the workgroups that free up first, which keeps the longest-first order of
+// the list effective at the end; early enough to hide the claim and the
+// lookup), and its last tile iteration issues the copies of that item's
+// first tile: the cache stream does not stop between items, and only the
+// next queries' latency remains at an item boundary.  Only cache layouts
+// whose full tiles need no LDS table take this form (contiguous, or paged
+// with power-of-two blocks of at least one copy instruction's rows).
+template <class F, class Attn>
+__device__ __forceinline__ void gqa_persistent_body(const DecodeArgs& a) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: wave-derived values in SGPRs
+
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[2][kGqaStageBytes];
+  __shared__ int4 s_item;
+
+  const int n_items = a.items_ctl[0];
+  int* const claim = a.items_ctl + 1;
+  const int4 none = make_int4(-1, 0, 0, 0);
+  auto lookup = [&](int t) __attribute__((always_inline)) { return t < n_items ? a.items[t] : none; };
+  auto published = [&]() __attribute__((always_inline)) {
+    const int4 v = s_item;
+    return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                     __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+  };
+
+  if (tid == 0) s_item = lookup(atomicAdd(claim, 1));
+  __syncthreads();
+  int4 cur = published();
+  if (cur.x < 0) return;
+
+  auto stage = [&](uint32_t t) __attribute__((always_inline)) { return (uint32_t)(uintptr_t)&ring[t & 1][0]; };
+  uint32_t gt = 0;          // tiles this workgroup has consumed; tile gt sits in stage gt & 1
+  bool head_issued = false; // the current item's first tile is already in flight
+  GqaCopier<F> cp(a, gqa_item_work<F::kTile>(a, cur, false), nullptr, wave, tid);
+  while (true) {
+    const GqaWork w = gqa_item_work<F::kTile>(a, cur, true);
+    Attn attn(a, w, wave, tid & 63);  // fetches the queries
+    cp.bind(w);
+    if (!head_issued) cp.issue(w.t_begin, stage(gt));
+    // Queries, the window bound and the first tile land here (a visible
+    // wait, so that the compiler places none inside the loop).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // The next item: thread 0 claims it at iteration c, looks it up at c+1
+    // and publishes it at c+2; every wave reads it at c+3, the last iteration
+    // of an item of four tiles or more.
+    const int n = w.n_tiles;
+    const int c = n > 4 ? n - 4 : 0;
+    int ticket = n_items;
+    int4 looked = none, nxt = none;
+    for (int it = 0; it < n; ++it) {
+      wait_copies_and_sync<0>();
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // nothing is in flight: the claim and lookup below have landed
+      if (it == c + 3) nxt = published();
+      if (tid == 0) {
+        if (it == c) ticket = atomicAdd(claim, 1);
+        if (it == c + 1) looked = lookup(ticket);
+        if (it == c + 2) s_item = looked;
+      }
+      if (it + 1 < n) {
+        cp.issue(w.t_begin + (it + 1) * F::kTile, stage(gt + 1));
+      } else if (nxt.x >= 0) {
+        const GqaWork wn = gqa_item_work<F::kTile>(a, nxt, false);
+        cp.bind(wn);
+        cp.issue(wn.t_begin, stage(gt + 1));
+      }
+      attn.tile(ring[gt & 1], w.t_begin + it * F::kTile, w.t_end, w.t_lo);
+      ++gt;
+    }
+    // The last tile's stage is free for the token-split merge; the other one
+    // receives the next item's first tile.
+    attn.finish(a, w, ring[(gt - 1) & 1], wave);
+    head_issued = nxt.x >= 0;
+    if (n < c + 4) {
+      // An item of fewer than four tiles ends before the next one is known.
+      if (tid == 0) {
+        if (n < c + 2) looked = lookup(ticket);
+        if (n < c + 3) s_item = looked;
+      }
+      __syncthreads();
+      nxt = published();
+      __syncthreads();  // s_item is rewritten during the next item
+    }
+    if (nxt.x < 0) break;
+    cur = nxt;
+  }
 }
 
 }  // namespace kvattn

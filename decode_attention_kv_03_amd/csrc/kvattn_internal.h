@@ -17,6 +17,7 @@ constexpr int kMaxGroupF32 = 64;   // largest h/g of the fp32 kernel
 constexpr int kMaxGroupBf16 = 128; // largest h/g of the bf16 kernel
 constexpr int kMaxMlaHeads = 128;
 constexpr float kLog2eHost = 1.4426950408889634f;
+constexpr int kPersistentWorkgroups = 512;  // persistent GQA grid: two resident workgroups per compute unit
 
 // One decode call, as the kernels see it.  Cache addressing:
 //   contiguous: row (b, j, t) at ((b * g + j) * cache_len + t) * width
@@ -62,6 +63,12 @@ struct DecodeArgs {
   // whose columns 512.. hold the shared RoPE key.
   const void* rope;
   int32_t rec_len;
+  // GQA work list of the persistent split kernel (null: one workgroup per
+  // split), written on the device by the plan kernel (gqa_plan.hip):
+  //   items[k] = (unit b * g + j, split, first token, end token), k < items_ctl[0];
+  //   items_ctl[1] = the claim counter (zero when the split kernel starts).
+  const int4* items;
+  int32_t* items_ctl;
   // Measurement only (MLA): when non-null, the first wave of workgroup 0
   // stores {s_memtime, s_memrealtime} at the start and at the end of its tile
   // loop here (four uint64 values).
@@ -96,6 +103,21 @@ struct MlaPlanArgs {
   int32_t* plan_count;
 };
 
+// Arguments of the GQA plan kernel: the work list of the persistent split
+// kernel for a call of `units` = batch * g (sequence, KV head) pairs cut into
+// splits of `split` tokens (at most n_split per pair).
+struct GqaPlanArgs {
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t g;
+  int32_t len_cap;
+  int32_t window;
+  int32_t split;
+  int32_t n_split;
+  int4* items;
+  int32_t* ctl;             // [0]: number of items, [1]: claim counter (set to 0)
+};
+
 // Optional events recorded when a launch's kernel starts and ends (null: none).
 struct LaunchEvents {
   hipEvent_t start = nullptr;
@@ -126,6 +148,7 @@ hipError_t launch_gqa_bf16(const DecodeArgs& a, hipStream_t stream, const Launch
 hipError_t launch_gqa_fp8(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_mla_bf16(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t stream);
+hipError_t launch_gqa_plan(const GqaPlanArgs& p, hipStream_t stream);
 hipError_t launch_mla_merge_pieces(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream);
 hipError_t launch_mla_explicit_attend(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);

@@ -38,8 +38,8 @@ _TAG = re.compile(r"<!-- kvattn-traffic (.*?) -->")
 # includes, and the split planning that sets its grid.
 _COMMON = ["plan.h", "kvattn_internal.h", "device_common.h", "lds_copy.h", "cache_addr.h"]
 KERNEL_SOURCES = {
-    "gqa_split_bf16": ["gqa_bf16.hip", "gqa_split.h", "merge.hip"] + _COMMON,
-    "gqa_split_fp8": ["gqa_fp8.hip", "gqa_split.h", "merge.hip"] + _COMMON,
+    "gqa_split_bf16": ["gqa_bf16.hip", "gqa_split.h", "gqa_plan.hip", "merge.hip"] + _COMMON,
+    "gqa_split_fp8": ["gqa_fp8.hip", "gqa_split.h", "gqa_plan.hip", "merge.hip"] + _COMMON,
     "gqa_split_f32": ["gqa_f32.hip", "merge.hip"] + _COMMON,
     "mla_split_bf16": ["mla_bf16.hip", "mla_plan.hip"] + _COMMON,
 }

@@ -69,6 +69,16 @@
  *    Its contents need no initialisation.  One workspace serves one call at
  *    a time: calls that share it must be ordered (for example, on one
  *    stream).
+ *  - A bf16 or fp8 GQA call with more than 2048 (sequence, KV head, split)
+ *    slots, on a contiguous cache or a paged one whose block size is a power
+ *    of two of at least 4 (bf16) or 8 (fp8) tokens, runs in a persistent
+ *    form when the workspace it is given also holds a list of the splits
+ *    that hold tokens (16 bytes per slot, after the partials: the size
+ *    kvattn_gqa_workspace_bytes reports always leaves room for it).  A
+ *    device-side kernel makes the list from seq_lens, and 512 resident
+ *    workgroups take its entries from a counter kept in the workspace.  Each
+ *    split is computed as in the one-workgroup-per-split form, so the
+ *    results are identical.
  */
 #ifndef KVATTN_H
 #define KVATTN_H

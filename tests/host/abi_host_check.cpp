@@ -36,6 +36,31 @@ static kvattn_status gqa_window(int32_t B, int32_t h, int32_t g, int32_t S, int3
                                   0.1f, window, dt, split, ws ? P : nullptr, ws, nullptr);
 }
 
+// The persistent form's work list: taken exactly when the grid of splits is large, for a bf16 cache with a
+// layout whose full tiles need no LDS table; it lies inside the workspace after the partials, one int4 per
+// possible item, then its count and claim counter; the plan kernel gets the call's split geometry.
+static void check_work_list(const kvattn::DecodeArgs& a, int32_t B, int32_t h, int32_t g, int32_t bs, int32_t W,
+                            int32_t S, size_t ws) {
+  const int64_t slots = (int64_t)B * g * a.n_split;
+  const bool pow2_ok = bs == 0 || (bs >= 4 && (bs & (bs - 1)) == 0);
+  const bool expect = a.n_split > 1 && slots > 4 * kvattn::kPersistentWorkgroups && pow2_ok;
+  CHECK((a.items != nullptr) == expect, "B=%d g=%d bs=%d n_split=%d: work list %d", B, g, bs, a.n_split,
+        a.items != nullptr);
+  CHECK(stub::last.gqa_plans == (expect ? 1 : 0), "plan launches %d", stub::last.gqa_plans);
+  if (!expect) return;
+  const auto* base = static_cast<const unsigned char*>(P);
+  const auto* part_end = reinterpret_cast<const unsigned char*>(a.part_lse) + (size_t)B * h * a.n_split * 4;
+  const auto* items = reinterpret_cast<const unsigned char*>(a.items);
+  const auto* ctl = reinterpret_cast<const unsigned char*>(a.items_ctl);
+  CHECK(reinterpret_cast<const unsigned char*>(a.part_o) == base, "partials first");
+  CHECK(items >= part_end && items + slots * 16 <= ctl && ctl + 8 <= base + ws, "work list outside the workspace");
+  CHECK((uintptr_t)(items - base) % 16 == 0 && (uintptr_t)(ctl - base) % 4 == 0, "alignment");
+  const kvattn::GqaPlanArgs& p = stub::last.gqa_plan;
+  CHECK(p.items == a.items && p.ctl == a.items_ctl && p.seq_lens == a.seq_lens, "plan pointers");
+  CHECK(p.batch == B && p.g == g && p.split == a.split_tokens && p.n_split == a.n_split && p.window == W &&
+            p.len_cap == S, "plan geometry");
+}
+
 static void window_sweep() {
   // A window call accepts exactly the bytes kvattn_gqa_workspace_bytes reports for the same arguments
   // (the query takes no window), and its splits cover the window's span.
@@ -67,6 +92,7 @@ static void window_sweep() {
               const size_t need = a.n_split > 1 ? (size_t)B * hg[0] * a.n_split * 129 * 4 : 0;
               CHECK(need <= ws, "need %zu > queried %zu", need, ws);
               CHECK(stub::last.merges == (a.n_split > 1 ? 1 : 0), "merge count");
+              check_work_list(a, B, hg[0], hg[1], bs, W, S, ws);
             }
 }
 

@@ -27,6 +27,12 @@ hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t) {
   ++stub::last.launches;
   return hipSuccess;
 }
+hipError_t launch_gqa_plan(const GqaPlanArgs& p, hipStream_t) {
+  stub::last.gqa_plan = p;
+  ++stub::last.gqa_plans;
+  ++stub::last.launches;
+  return hipSuccess;
+}
 hipError_t launch_mla_merge_pieces(const DecodeArgs&, hipStream_t) {
   ++stub::last.launches;
   return hipSuccess;

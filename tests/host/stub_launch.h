@@ -8,6 +8,8 @@ struct Record {
   const char* kernel = nullptr;
   kvattn::DecodeArgs args{};
   kvattn::MlaPlanArgs plan{};
+  kvattn::GqaPlanArgs gqa_plan{};
+  int gqa_plans = 0;
   kvattn::ProjectArgs projects[2]{};
   int n_projects = 0;
   struct Transpose {
