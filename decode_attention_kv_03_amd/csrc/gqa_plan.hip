@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kClasses = 32;
+constexpr int kCachedRounds = 4;  // rounds of units whose spans stay in registers between the passes
 
 // Length class of a last split holding `rest` tokens, 0 < rest < split:
 // ceil(32 * rest / split), in 1 .. 32.
@@ -77,14 +78,19 @@ __global__ __launch_bounds__(kThreads) void gqa_plan(GqaPlanArgs p) {
   __syncthreads();
 
   // Full splits, in unit order; the short last splits are counted per class.
+  // The spans of the first kCachedRounds rounds of units stay in registers.
+  UnitSpan cached[kCachedRounds];
   int carry = 0;
-  for (int u0 = 0; u0 < units; u0 += kThreads) {
+  for (int u0 = 0, i = 0; u0 < units; u0 += kThreads, ++i) {
     const int u = u0 + tid;
     UnitSpan r{0, 0, 0, 0};
     if (u < units) {
       r = unit_span(p, u);
       if (r.rest > 0) atomicAdd(&s_next[length_class(r.rest, p.split)], 1);
     }
+#pragma unroll
+    for (int k = 0; k < kCachedRounds; ++k)
+      if (k == i) cached[k] = r;
     int total;
     const int first = carry + block_exclusive_scan(r.full, s_wave, total);
     for (int s = 0; s < r.full; ++s) {
@@ -94,21 +100,32 @@ __global__ __launch_bounds__(kThreads) void gqa_plan(GqaPlanArgs p) {
     carry += total;
   }
   __syncthreads();
-  // Slots of the short splits: the longest class first.
-  if (tid == 0) {
-    int pos = carry;
-    for (int c = kClasses; c >= 1; --c) {
-      const int n = s_next[c];
-      s_next[c] = pos;
-      pos += n;
+  // Slots of the short splits, the longest class first: an exclusive scan
+  // over the classes in descending order, on the first wave.
+  if (tid < 64) {
+    const int c = kClasses - tid;  // lanes 0 .. 31: classes 32 .. 1
+    const int n = c >= 1 ? s_next[c] : 0;
+    int x = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (tid >= d) x += y;
     }
-    p.ctl[0] = pos;
-    p.ctl[1] = 0;
+    if (c >= 1) s_next[c] = carry + x - n;
+    if (tid == 63) {
+      p.ctl[0] = carry + x;
+      p.ctl[1] = 0;
+    }
   }
   __syncthreads();
-  for (int u = tid; u < units; u += kThreads) {
-    const UnitSpan r = unit_span(p, u);
-    if (r.rest > 0) {
+  for (int u0 = 0, i = 0; u0 < units; u0 += kThreads, ++i) {
+    const int u = u0 + tid;
+    UnitSpan r{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kCachedRounds; ++k)
+      if (k == i) r = cached[k];
+    if (i >= kCachedRounds && u < units) r = unit_span(p, u);
+    if (u < units && r.rest > 0) {
       const int slot = atomicAdd(&s_next[length_class(r.rest, p.split)], 1);
       const int t0 = r.base + r.full * p.split;
       p.items[slot] = make_int4(u, r.full, t0, r.len);
