@@ -38,6 +38,12 @@
 //    split the heads when it has more;
 //  * the split's result is either the final output (one split) or a partial
 //    rounded to bf16 plus its fp32 log2-domain log-sum-exp for the merge.
+//
+// A call whose grid of splits would run in many rounds (ragged or paged
+// batches) takes the persistent form at the end of this file instead: 512
+// resident workgroups take the splits that hold tokens from a device-side
+// list (gqa_plan.hip) and compute each exactly as above, streaming from one
+// split into the next without a start-up pause.
 #pragma once
 
 #include "device_common.h"
