@@ -180,6 +180,7 @@ GqaPersistentLayout gqa_persistent_layout(CacheKind kind, int64_t batch, int64_t
   const int64_t slots = batch * g * nsplit;
   const int32_t min_shift = kind == CacheKind::kFp8E4m3 ? 3 : 2;
   if (kind == CacheKind::kF32 || nsplit <= 1 || slots <= 4 * kvattn::kPersistentWorkgroups) return l;
+  if (slots > INT32_MAX / 2) return l;  // the device plan counts items in 32-bit integers
   if (block_size > 0 && pow2_shift(block_size) < min_shift) return l;
   l.items = (size_t)round_up((int64_t)partials, 256);
   l.ctl = l.items + (size_t)round_up(slots * 16, 256);
