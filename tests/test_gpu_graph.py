@@ -106,3 +106,22 @@ def test_mla_call_replays_in_a_graph():
     ref, _ = oracle.mla_absorbed_decode(W.host_view(x["q"]), W.host_view(x["cache"]), lens, w.scale, bf16=True)
     got = out.double().cpu().numpy()
     assert np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref))
+
+
+def test_persistent_gqa_call_replays_in_a_graph():
+    """The persistent form's claim counter sits in the workspace and is reset by its plan kernel on every replay."""
+    from tests.test_gpu_edges import gqa_reference
+    from tests.test_gpu_persistent import PERSISTENT_SLOTS, n_split
+
+    B, h, g, S, bs, split = 40, 32, 8, 3000, 16, 64
+    rng = np.random.default_rng(17)
+    lens = np.concatenate([[0, 1, 64, S], rng.integers(0, S + 1, B - 4)]).astype(np.int32)
+    w = W.GqaWorkload("graph_persistent", B, h, g, 128, S, "bf16", 23, 1 / np.sqrt(128), block_size=bs)
+    x = W.make_gqa_inputs(w, DEV, lens=lens, poison_tail=True)
+    max_len = x["block_table"].shape[1] * bs
+    assert B * g * n_split(w, max_len, split) > PERSISTENT_SLOTS, "case does not reach the persistent form"
+    note(f"graph gqa persistent form: paged bs={bs} B={B} h={h} g={g} split={split}")
+    out = _replay_matches_eager(_Gqa(x, w, split), x["q"], n_replays=4, seed=3)
+    ref, _ = gqa_reference(x)
+    got = out.double().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= ATOL + RTOL * np.abs(ref))
