@@ -166,3 +166,24 @@ def test_persistent_through_the_no_allocation_entry_point():
     torch.cuda.synchronize()
     ref_s, _ = gqa_reference(xs)
     assert_close(out_s.float().cpu().numpy(), ref_s, "after")
+
+
+def test_more_units_than_the_plan_keeps_in_registers():
+    """The plan keeps the spans of its first 4096 (sequence, KV head) units in registers and recomputes the rest."""
+    B, h, g, S, bs, split = 520, 64, 8, 256, 16, 64
+    assert B * g > 4 * 1024
+    rng = np.random.default_rng(11)
+    lens = lens_with_edges(rng, B, S)
+    w, x, max_len = inputs("many_units", B, h, g, S, "bf16", 61, lens, bs)
+    assert B * g * n_split(w, max_len, split) > PERSISTENT_SLOTS
+    note(f"{B * g} units: B={B} h={h} g={g} S={S} bs={bs} split={split}")
+    out, lse = gqa_call(x, return_lse=True, split_tokens=split)
+    torch.cuda.synchronize()
+    ref, ref_lse = gqa_reference(x)
+    assert_close(out.float().cpu().numpy(), ref, "many_units")
+    got = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    np.testing.assert_allclose(got[fin], ref_lse[fin], atol=LSE_ATOL, rtol=1e-4)
+    out_g, lse_g = grid_form_call(x, max_len, split, 0, B * h * n_split(w, max_len, split) * (128 * 2 + 4))
+    assert torch.equal(out_g, out) and torch.equal(lse_g, lse)
