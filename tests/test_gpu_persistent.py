@@ -6,9 +6,10 @@ contiguous cache or on power-of-two blocks of at least one copy
 instruction's rows, runs as 512 resident workgroups that take the splits
 holding tokens from a device-side list.  Checked here through the C ABI:
 
-* every group shape (h/g = 4, 8, 32, 64, 128), contiguous and paged, bf16 and
-  fp8, a sliding window, zero and one-token lengths, and fewer items than
-  resident workgroups, against the fp64 oracle;
+* every group shape (h/g = 4, 8, 32, 64, 128), contiguous and paged (down to
+  4-token bf16 and 8-token fp8 blocks), bf16 and fp8, a sliding window, zero
+  and one-token lengths, fewer items than resident workgroups, and more units
+  than the plan keeps in registers, against the fp64 oracle;
 * bit-identical outputs to the grid-per-split form of the same call (a
   workspace with no room for the list keeps that form), over reruns, and
   through the no-allocation entry point.
@@ -96,6 +97,9 @@ CASES = [
     ("paged_fp8_r4", 32, 32, 8, 4000, "fp8", 16, 128, 0),
     ("paged_window", 64, 32, 8, 6000, "bf16", 16, 64, 700),
     ("fp8_window", 40, 64, 8, 5000, "fp8", 0, 128, 900),
+    # the smallest blocks that take the persistent form: one copy instruction's rows
+    ("paged_bs4", 48, 32, 8, 2000, "bf16", 4, 64, 0),
+    ("paged_fp8_bs8", 48, 32, 8, 2000, "fp8", 8, 128, 0),
 ]
 
 
