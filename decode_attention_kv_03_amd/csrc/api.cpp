@@ -308,19 +308,22 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
 
 // Reconstruct-then-attend MLA: the two weights transposed ([h, 128, 512] bf16
 // each, so that the projections read both operands row-wise), per-head K and
-// V rows rebuilt from the latent cache ([B, h, max_seq_len, 128] bf16 each),
-// then the split partials (bf16 outputs, fp32 log-sum-exps), each region
-// 256-byte aligned.  Sizes in 128-bit arithmetic; total 0 when they overflow
-// (the caller rejects it).
+// V rows rebuilt from the latent cache ([B, h, R, 128] bf16 each, R =
+// max_seq_len rounded up to the rebuild's 256-row tiles; rows from
+// max_seq_len on are never read), then the split partials (bf16 outputs,
+// fp32 log-sum-exps), each region 256-byte aligned.  Sizes in 128-bit
+// arithmetic; total 0 when they overflow (the caller rejects it).
 struct ExplicitWorkspace {
   size_t wt_k, wt_v, kc, v, part_o, part_lse, total;
 };
 constexpr int32_t kExplicitHead = 128;  // reconstructed content-key and value width
+constexpr int32_t kRebuildRows = 256;   // rows per tile of the rebuild projection
+int64_t rebuilt_rows(int64_t max_seq_len) { return round_up(max_seq_len, kRebuildRows); }
 ExplicitWorkspace explicit_workspace(int64_t batch, int64_t heads, int64_t max_seq_len, int64_t nsplit) {
   typedef unsigned __int128 u128;
   auto up = [](u128 x) { return (x + 255) / 256 * 256; };
   const u128 wt = up((u128)heads * kvattn::kMlaLatent * kExplicitHead * 2);
-  const u128 rows = (u128)batch * heads * (u128)max_seq_len;
+  const u128 rows = (u128)batch * heads * (u128)rebuilt_rows(max_seq_len);
   const u128 rec = up(rows * kExplicitHead * 2);
   const u128 po = nsplit > 1 ? up((u128)batch * heads * nsplit * kExplicitHead * 2) : 0;
   const u128 pl = nsplit > 1 ? up((u128)batch * heads * nsplit * 4) : 0;
@@ -640,7 +643,7 @@ kvattn_status kvattn_mla_explicit_decode(const void* q, const void* cache, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   const int64_t row_elems = kvattn::kMlaRow;
-  const int64_t rec = (int64_t)max_seq_len * kExplicitHead;  // elements of one (sequence, head) block
+  const int64_t rec = rebuilt_rows(max_seq_len) * kExplicitHead;  // elements of one (sequence, head) block
   if (max_seq_len > 0) {
     // k_i = c W_uk^(i) and v_i = c W_uv^(i) for every (sequence, head, row < max_seq_len), with the
     // weights first transposed to [h, 128, 512] so that both operands are read row-wise.
@@ -651,17 +654,17 @@ kvattn_status kvattn_mla_explicit_decode(const void* q, const void* cache, const
                                          kExplicitHead, cache_len * row_elems, 0, row_elems,
                                          (int64_t)d_latent * kExplicitHead, true, num_heads * rec, rec,
                                          kExplicitHead);
-    if ((e = kvattn::launch_latent_project(p, s)) != hipSuccess) return hip_status(e, "projection kernel launch");
+    if ((e = kvattn::launch_latent_rebuild(p, s)) != hipSuccess) return hip_status(e, "projection kernel launch");
     p.w = reinterpret_cast<const uint16_t*>(ws + wl.wt_v);
     p.y = reinterpret_cast<uint16_t*>(ws + wl.v);
-    if ((e = kvattn::launch_latent_project(p, s)) != hipSuccess) return hip_status(e, "projection kernel launch");
+    if ((e = kvattn::launch_latent_rebuild(p, s)) != hipSuccess) return hip_status(e, "projection kernel launch");
   }
   kvattn::DecodeArgs a{};
   a.q = q;
   a.k = ws + wl.kc;
   a.v = ws + wl.v;
   a.rope = cache;
-  a.rec_len = max_seq_len;
+  a.rec_len = (int32_t)rebuilt_rows(max_seq_len);
   a.seq_lens = seq_lens;
   a.out = out;
   a.lse = lse;

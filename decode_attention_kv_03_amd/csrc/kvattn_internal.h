@@ -151,6 +151,10 @@ hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t stream);
 hipError_t launch_gqa_plan(const GqaPlanArgs& p, hipStream_t stream);
 hipError_t launch_mla_merge_pieces(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream);
+// The same projection for the naive MLA form's K and V rebuild (transposed
+// weights stacked over an even number of heads of 128 columns, y_head room
+// for `rows` rounded up to 256: whole 256-row tiles are written), else as above.
+hipError_t launch_latent_rebuild(const ProjectArgs& p, hipStream_t stream);
 hipError_t launch_mla_explicit_attend(const DecodeArgs& a, hipStream_t stream, const LaunchEvents& ev);
 // W^(i) [rows, cols] -> W^(i)^T [cols, rows] for every head (bf16; rows, cols multiples of 64).
 hipError_t launch_transpose_heads(const void* src, void* dst, int heads, int rows, int cols, hipStream_t stream);

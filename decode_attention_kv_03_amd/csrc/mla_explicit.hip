@@ -197,6 +197,212 @@ __global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
   }
 }
 
+// Rebuild projection of the naive form: Y[o, i, s, :] = X[o, s, :] W^(i) for
+// every head i, with the weights already transposed to W^(i)^T [128, K] and
+// stored one head after another.  Those rows are then one [heads * 128, K]
+// operand, so the projection of one outer index is a single GEMM over all
+// heads, and a 256 x 256 output tile spans two heads.  The tile size is what
+// sets the rate here: with K = 512 a 128 x 128 tile reads 64 operand bytes
+// per MFMA clock of a compute unit, as much as one compute unit can load;
+// a 256 x 256 tile needs half of that.
+//
+// Persistent: one workgroup of eight waves (two per SIMD) per compute unit
+// walks its share of the tiles.  It computes Y^T = W^T X^T on
+// v_mfma_f32_16x16x32_bf16, wave w the 128 (columns) x 64 (rows) block at
+// columns 128 (w / 4), rows 64 (w % 4): 32 accumulators of four per lane.
+// K runs in steps of 32 through a four-stage LDS ring filled by direct
+// global -> LDS copies (global_load_lds_dwordx4, with no cache hint: every
+// operand tile is read by many workgroups), three steps in flight, and the
+// steps of consecutive tiles form one stream, so the next tile's first steps
+// are in flight while a tile's results are written.  A step's operands are
+// 16-row blocks of 1 KiB (16 rows x 64 bytes): copy lane l fills row l/4,
+// physical chunk l%4, which holds logical chunk (l%4) ^ ((l/4 / 2) % 4), so
+// the fragment reads (row l%16, logical chunk l/16) fall on distinct bank
+// slots.  The results leave through a staging area of 4 KiB per wave apart
+// from the ring, 32 columns at a time, as 64-byte row pieces; their stores
+// stay in flight during the next tile.  Every tile writes all of its 256
+// rows (y holds `rows` rounded up to 256 per outer index and head; rows past
+// `rows` are computed from copies of the last one), so each tile issues
+// exactly 16 stores per wave, which the waits below count: loads, stores
+// and LDS copies of a wave retire in issue order.
+//
+// Tile order: XCD x (workgroups x, x + 8, ...) takes the x-th eighth of the
+// tile sequence, its 32 workgroups in turn, so the tiles an XCD runs
+// together are 32 consecutive ones.  The sequence runs over groups of four
+// row tiles, column tiles outer and row tiles inner within a group, so those
+// 32 tiles are four row tiles by eight column tiles, whose operands (1 MiB of
+// X, 2 MiB of W) stay in the XCD's L2.
+constexpr int kRbM = 256, kRbN = 256, kRbK = 32, kRbStages = 4;
+constexpr int kRbOpBytes = kRbM * kRbK * 2;    // one operand's 256 rows for one K step: 16 KiB
+constexpr int kRbStageBytes = 2 * kRbOpBytes;  // X rows, then W rows
+constexpr int kRbWaves = 8;
+constexpr int kRbStgBytes = 64 * 64;           // per wave: 64 rows x 32 bf16 columns
+constexpr int kRbGroupM = 4;                   // row tiles per group of the tile order
+constexpr int kRbSlots = 32;                   // workgroups per XCD (one per compute unit)
+constexpr int kRbStores = 16;                  // output stores per wave and tile
+constexpr int kRbCopies = 4;                   // copies per wave and K step
+
+// 16-byte global -> LDS copy of every lane (lane i's bytes land at lds_base +
+// 16 i; lds_base through M0, which nothing else in this kernel writes), with
+// the default cache policy.  The compiler does not see it in the vector-
+// memory counter; the loop waits for the copies explicitly.
+__device__ __forceinline__ void rb_copy(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// At most n of this wave's vector-memory operations outstanding (n is one of
+// the counts the loop can need: copies of up to two later steps, plus the 16
+// stores of one tile), then a workgroup barrier.
+__device__ __forceinline__ void rb_wait_sync(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 20: asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  }
+}
+
+// Staging address of 16-byte chunk `chunk` of row `row` (64-byte rows, the
+// chunk XORed with (row / 4) % 4: 16 consecutive rows at one chunk, or 4
+// rows at all four, fall on distinct bank slots).
+__device__ __forceinline__ int rb_stg_off(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+__global__ __launch_bounds__(kRbWaves * 64, 1) void latent_rebuild(ProjectArgs p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kRbStages * kRbStageBytes + kRbWaves * kRbStgBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int m_per_outer = (p.rows + kRbM - 1) / kRbM;
+  const int m_all = p.outer * m_per_outer;
+  const int n_tiles = p.heads * p.n_dim / kRbN;
+  const int64_t total = (int64_t)m_all * n_tiles;
+  const int64_t per_xcd = (total + 7) / 8;
+  const int64_t first = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int64_t end = min(total, (int64_t)((blockIdx.x & 7) + 1) * per_xcd);
+  if (first >= end) return;
+  const int my_tiles = (int)((end - first + kRbSlots - 1) / kRbSlots);  // tiles first, first + 32, ...
+  const int nk = p.k_dim / kRbK;
+  const int steps = my_tiles * nk;
+
+  // Operand rows and output base of this workgroup's i-th tile.
+  const int rr = lane >> 2, lc = (lane & 3) ^ ((rr >> 1) & 3);
+  const int wn = wave >> 2, wm = wave & 3;
+  struct Tile {
+    const uint16_t* xs[2];
+    const uint16_t* ws[2];
+    uint16_t* y;  // row m0 + 64 wm, column 0 of this wave's head
+  };
+  auto tile_of = [&](int i) __attribute__((always_inline)) {
+    const int64_t t = first + (int64_t)kRbSlots * i;
+    const int64_t group = (int64_t)kRbGroupM * n_tiles;
+    const int first_m = (int)(t / group) * kRbGroupM;
+    const int gm = min(m_all - first_m, kRbGroupM);
+    const int r = (int)(t % group);
+    const int mt = first_m + r % gm, nt = r / gm;
+    const int o = mt / m_per_outer;
+    const int m0 = (mt % m_per_outer) * kRbM, n0 = nt * kRbN;
+    Tile T;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 16 * (2 * wave + j) + rr;
+      T.xs[j] = p.x + (int64_t)o * p.x_outer + (int64_t)min(m0 + row, p.rows - 1) * p.x_row + 8 * lc;
+      T.ws[j] = p.w + (int64_t)(n0 + row) * p.k_dim + 8 * lc;
+    }
+    T.y = p.y + (int64_t)o * p.y_outer + (int64_t)((n0 + 128 * wn) / p.n_dim) * p.y_head +
+          (int64_t)(m0 + 64 * wm) * p.y_row;
+    return T;
+  };
+
+  // Step G (tile G / nk, K step G % nk) into stage G % 4: wave w fills
+  // 16-row blocks 2w and 2w+1 of both operands.
+  Tile iss = tile_of(0);
+  auto issue = [&](int G) __attribute__((always_inline)) {
+    const int kt = G % nk;
+    if (kt == 0 && G > 0) iss = tile_of(G / nk);
+    const uint32_t base = (uint32_t)(uintptr_t)&lds[(G % kRbStages) * kRbStageBytes] + 2 * wave * 1024;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) rb_copy(iss.xs[j] + kt * kRbK, base + j * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) rb_copy(iss.ws[j] + kt * kRbK, base + kRbOpBytes + j * 1024);
+  };
+
+  // Fragments: lane l reads row l%16 of a block at logical chunk l/16 (the
+  // eight k of v_mfma_f32_16x16x32_bf16's A and B operands).
+  const int n16 = lane & 15, g = lane >> 4;
+  const int koff = n16 * 64 + ((g ^ ((n16 >> 1) & 3)) << 4);
+  f32x4 acc[8][4];
+  auto zero = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto compute = [&](int stage) __attribute__((always_inline)) {
+    const unsigned char* s = lds + stage * kRbStageBytes;
+    bf16x8 xf[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      xf[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s + (4 * wm + mb) * 1024 + koff));
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const bf16x8 wf =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s + kRbOpBytes + (8 * wn + nb) * 1024 + koff));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[mb], acc[nb][mb], 0, 0, 0);
+    }
+  };
+
+  // acc[nb][mb][v] = Y^T[column 16 nb + 4 (lane/16) + v][row 16 mb + lane%16]
+  // of the wave's block; written 32 columns (two nb) at a time through the
+  // wave's own staging rows, 16 stores per wave.
+  unsigned char* stg = lds + kRbStages * kRbStageBytes + wave * kRbStgBytes;
+  auto write_tile = [&](uint16_t* y) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int nbi = 0; nbi < 2; ++nbi)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const f32x4& a = acc[2 * q + nbi][mb];
+          *reinterpret_cast<uint2*>(stg + rb_stg_off(16 * mb + n16, 2 * nbi + (g >> 1)) + 8 * (g & 1)) =
+              make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's staged rows have landed
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = 16 * u + (lane >> 2), c = lane & 3;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rb_stg_off(row, c));
+        *reinterpret_cast<u32x4*>(y + (int64_t)row * p.y_row + 32 * q + 8 * c) = v;
+      }
+    }
+  };
+
+  // Step G: wait for its copies (those of the next two steps, and the stores
+  // of a tile that ended since G's copies were issued, may stay in flight)
+  // and for every wave to finish step G-1, whose stage then takes step G+3.
+  zero();
+#pragma unroll
+  for (int G = 0; G < kRbStages - 1; ++G)
+    if (G < steps) issue(G);
+  for (int G = 0; G < steps; ++G) {
+    const int later_copies = kRbCopies * min(2, steps - 1 - G);
+    // A tile ended after step G'' in [G-3, G-1] when G'' % nk == nk - 1: then G % nk < 3, and G >= nk.
+    const int later_stores = (G >= nk && G % nk < kRbStages - 1) ? kRbStores : 0;
+    rb_wait_sync(later_copies + later_stores);
+    if (G + kRbStages - 1 < steps) issue(G + kRbStages - 1);
+    compute(G % kRbStages);
+    if (G % nk == nk - 1) {
+      write_tile(tile_of(G / nk).y);
+      zero();
+    }
+  }
+}
+
 // W^(i) [rows, cols] -> W^(i)^T [cols, rows] for every head, through a
 // 64 x 64 LDS tile (bf16; rows and cols multiples of 64).
 __global__ __launch_bounds__(256) void transpose_heads(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
@@ -477,6 +683,20 @@ hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream) {
   if (blocks <= 0 || blocks > 0x7fffffff || p.k_dim % kBK != 0 || p.n_dim % kBN != 0) return hipErrorInvalidValue;
   if (p.w_transposed) latent_project<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
   else latent_project<false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_rebuild(const ProjectArgs& p, hipStream_t stream) {
+  // Stacked transposed weights of 128 columns per head, two heads per tile;
+  // anything else takes the general projection.
+  // The waits assume at least four K steps per tile (one tile end at most
+  // between a step's copies and its use), and y must hold whole 256-row tiles.
+  const int64_t padded_rows = ((int64_t)p.rows + kRbM - 1) / kRbM * kRbM;
+  if (!p.w_transposed || p.n_dim != 128 || p.heads % 2 != 0 || p.k_dim % kRbK != 0 || p.k_dim < 4 * kRbK ||
+      p.w_head != (int64_t)p.n_dim * p.k_dim || p.rows < 1 || p.outer < 1 || p.y_head < padded_rows * p.y_row ||
+      (int64_t)p.outer * ((p.rows + kRbM - 1) / kRbM) * (p.heads / 2) > INT32_MAX / 2)
+    return launch_latent_project(p, stream);
+  latent_rebuild<<<dim3(8 * kRbSlots), dim3(kRbWaves * 64), 0, stream>>>(p);
   return hipGetLastError();
 }
 

@@ -259,7 +259,8 @@ static void explicit_mla() {
                                            KVATTN_BF16, split, base, ws - 1, nullptr) == KVATTN_ERR_WORKSPACE,
                 "short explicit workspace");
           const kvattn::DecodeArgs& a = stub::last.args;
-          const int64_t rec = (int64_t)B * h * S * 128 * 2;
+          const int64_t R = (S + 255) / 256 * 256;  // rebuilt rows per (sequence, head): whole 256-row tiles
+          const int64_t rec = (int64_t)B * h * R * 128 * 2;
           const int64_t wbytes = (int64_t)h * 512 * 128 * 2;
           auto inside = [&](const void* p, int64_t bytes) {
             const unsigned char* c = static_cast<const unsigned char*>(p);
@@ -286,12 +287,12 @@ static void explicit_mla() {
               CHECK(reinterpret_cast<const void*>(stub::last.projects[tt].w) == tr.dst, "projection reads other weights");
             }
             CHECK(stub::last.transposes[0].dst != stub::last.transposes[1].dst, "weights share a region");
-            CHECK(pk.y_row == 128 && pk.y_head == (int64_t)S * 128 && pk.y_outer == (int64_t)h * S * 128, "y strides");
+            CHECK(pk.y_row == 128 && pk.y_head == R * 128 && pk.y_outer == (int64_t)h * R * 128, "y strides");
             CHECK(reinterpret_cast<const void*>(pk.y) == a.k && reinterpret_cast<const void*>(stub::last.projects[1].y) == a.v,
                   "attention reads other rows than the projections wrote");
             CHECK(pk.m_tiles == (S + 127) / 128 && pk.n_tiles == 1, "tiles");
           }
-          CHECK(a.rec_len == S && a.rope == P, "rope source");
+          CHECK(a.rec_len == R && a.rope == P, "rope source");
         }
   // projections: rejected shapes and strides
   auto proj = [&](int32_t k, int32_t n, int64_t xr, int64_t yr, const void* y = P) {

@@ -44,6 +44,7 @@ hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t) {
   ++stub::last.launches;
   return hipSuccess;
 }
+hipError_t launch_latent_rebuild(const ProjectArgs& p, hipStream_t s) { return launch_latent_project(p, s); }
 hipError_t launch_mla_explicit_attend(const DecodeArgs& a, hipStream_t, const LaunchEvents&) {
   return record("mla_explicit_attend", a);
 }

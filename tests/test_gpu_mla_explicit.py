@@ -157,6 +157,7 @@ def check_explicit(x, out, lse, rows=None):
     (3, 128, [1000, 1, 129], 0),
     (3, 8, [0, 64, 65], 64),
     (1, 128, [2048], 256),
+    (2, 5, [300, 17], 0),       # an odd number of heads: the general projection rebuilds the rows
 ])
 def test_explicit_decode_matches_oracle(B, h, lens, split):
     w = W.MlaWorkload(f"explicit_{B}_{h}", B, h, max(lens) + 3, 300 + h + B, 1 / np.sqrt(192), form="explicit")
