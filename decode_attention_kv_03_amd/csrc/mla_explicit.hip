@@ -224,7 +224,9 @@ __global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
 // rows (y holds `rows` rounded up to 256 per outer index and head; rows past
 // `rows` are computed from copies of the last one), so each tile issues
 // exactly 16 stores per wave, which the waits below count: loads, stores
-// and LDS copies of a wave retire in issue order.
+// and LDS copies of a wave retire from the vector-memory counter in issue
+// order (the compiler's own waits on this target rely on that too, e.g. a
+// load's value used with a later store and load still outstanding).
 //
 // Tile order: XCD x (workgroups x, x + 8, ...) takes the x-th eighth of the
 // tile sequence, its 32 workgroups in turn, so the tiles an XCD runs
