@@ -210,15 +210,16 @@ __global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
 // walks its share of the tiles.  It computes Y^T = W^T X^T on
 // v_mfma_f32_16x16x32_bf16, wave w the 128 (columns) x 64 (rows) block at
 // columns 128 (w / 4), rows 64 (w % 4): 32 accumulators of four per lane.
-// K runs in steps of 32 through a four-stage LDS ring filled by direct
+// K runs in steps of 64 through a two-stage LDS ring filled by direct
 // global -> LDS copies (global_load_lds_dwordx4, with no cache hint: every
-// operand tile is read by many workgroups), three steps in flight, and the
-// steps of consecutive tiles form one stream, so the next tile's first steps
-// are in flight while a tile's results are written.  A step's operands are
-// 16-row blocks of 1 KiB (16 rows x 64 bytes): copy lane l fills row l/4,
-// physical chunk l%4, which holds logical chunk (l%4) ^ ((l/4 / 2) % 4), so
-// the fragment reads (row l%16, logical chunk l/16) fall on distinct bank
-// slots.  The results leave through a staging area of 4 KiB per wave apart
+// operand tile is read by many workgroups), the next step in flight while a
+// step computes, and the steps of consecutive tiles form one stream, so the
+// next tile's first step is in flight while a tile's results are written.
+// A copy instruction fetches 8 whole 128-byte rows of a step (64 k): copy
+// lane l fills row l/8, physical chunk l%8, which holds logical chunk
+// (l%8) ^ ((row / 2) % 8), so the fragment reads (16 rows at one logical
+// chunk) fall on distinct bank slots.  (Steps of 32 k, half rows, fetched
+// every cache line twice, half of it each time.)  The results leave through a staging area of 4 KiB per wave apart
 // from the ring, 32 columns at a time, as 64-byte row pieces; their stores
 // stay in flight during the next tile.  Every tile writes all of its 256
 // rows (y holds `rows` rounded up to 256 per outer index and head; rows past
@@ -234,15 +235,15 @@ __global__ __launch_bounds__(256, 2) void latent_project(ProjectArgs p) {
 // row tiles, column tiles outer and row tiles inner within a group, so those
 // 32 tiles are four row tiles by eight column tiles, whose operands (1 MiB of
 // X, 2 MiB of W) stay in the XCD's L2.
-constexpr int kRbM = 256, kRbN = 256, kRbK = 32, kRbStages = 4;
-constexpr int kRbOpBytes = kRbM * kRbK * 2;    // one operand's 256 rows for one K step: 16 KiB
+constexpr int kRbM = 256, kRbN = 256, kRbK = 64, kRbStages = 2;
+constexpr int kRbOpBytes = kRbM * kRbK * 2;    // one operand's 256 rows for one K step: 32 KiB
 constexpr int kRbStageBytes = 2 * kRbOpBytes;  // X rows, then W rows
 constexpr int kRbWaves = 8;
 constexpr int kRbStgBytes = 64 * 64;           // per wave: 64 rows x 32 bf16 columns
 constexpr int kRbGroupM = 4;                   // row tiles per group of the tile order
 constexpr int kRbSlots = 32;                   // workgroups per XCD (one per compute unit)
 constexpr int kRbStores = 16;                  // output stores per wave and tile
-constexpr int kRbCopies = 4;                   // copies per wave and K step
+constexpr int kRbCopies = 8;                   // copies per wave and K step
 
 // 16-byte global -> LDS copy of every lane (lane i's bytes land at lds_base +
 // 16 i; lds_base through M0, which nothing else in this kernel writes), with
@@ -255,18 +256,12 @@ __device__ __forceinline__ void rb_copy(const void* src, uint32_t lds_base) {
                : "memory");
 }
 
-// At most n of this wave's vector-memory operations outstanding (n is one of
-// the counts the loop can need: copies of up to two later steps, plus the 16
-// stores of one tile), then a workgroup barrier.
+// At most n of this wave's vector-memory operations outstanding (0, or the
+// 16 stores of a tile that ended after the awaited copies were issued), then
+// a workgroup barrier.
 __device__ __forceinline__ void rb_wait_sync(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 16: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    case 20: asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
-  }
+  if (n == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Staging address of 16-byte chunk `chunk` of row `row` (64-byte rows, the
@@ -292,11 +287,11 @@ __global__ __launch_bounds__(kRbWaves * 64, 1) void latent_rebuild(ProjectArgs p
   const int steps = my_tiles * nk;
 
   // Operand rows and output base of this workgroup's i-th tile.
-  const int rr = lane >> 2, lc = (lane & 3) ^ ((rr >> 1) & 3);
+  const int rr = lane >> 3;  // row within a copy's 8 rows: row 8 (4 wave + j) + rr of the tile
   const int wn = wave >> 2, wm = wave & 3;
   struct Tile {
-    const uint16_t* xs[2];
-    const uint16_t* ws[2];
+    const uint16_t* xs[4];
+    const uint16_t* ws[4];
     uint16_t* y;  // row m0 + 64 wm, column 0 of this wave's head
   };
   auto tile_of = [&](int i) __attribute__((always_inline)) {
@@ -310,8 +305,9 @@ __global__ __launch_bounds__(kRbWaves * 64, 1) void latent_rebuild(ProjectArgs p
     const int m0 = (mt % m_per_outer) * kRbM, n0 = nt * kRbN;
     Tile T;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = 16 * (2 * wave + j) + rr;
+    for (int j = 0; j < 4; ++j) {
+      const int row = 8 * (4 * wave + j) + rr;
+      const int lc = (lane & 7) ^ ((row >> 1) & 7);
       T.xs[j] = p.x + (int64_t)o * p.x_outer + (int64_t)min(m0 + row, p.rows - 1) * p.x_row + 8 * lc;
       T.ws[j] = p.w + (int64_t)(n0 + row) * p.k_dim + 8 * lc;
     }
@@ -320,23 +316,26 @@ __global__ __launch_bounds__(kRbWaves * 64, 1) void latent_rebuild(ProjectArgs p
     return T;
   };
 
-  // Step G (tile G / nk, K step G % nk) into stage G % 4: wave w fills
-  // 16-row blocks 2w and 2w+1 of both operands.
+  // Step G (tile G / nk, K step G % nk) into stage G % 2: wave w fills rows
+  // 32w .. 32w+31 of both operands, 8 rows per copy.
   Tile iss = tile_of(0);
   auto issue = [&](int G) __attribute__((always_inline)) {
     const int kt = G % nk;
     if (kt == 0 && G > 0) iss = tile_of(G / nk);
-    const uint32_t base = (uint32_t)(uintptr_t)&lds[(G % kRbStages) * kRbStageBytes] + 2 * wave * 1024;
+    const uint32_t base = (uint32_t)(uintptr_t)&lds[(G % kRbStages) * kRbStageBytes] + 4 * wave * 1024;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) rb_copy(iss.xs[j] + kt * kRbK, base + j * 1024);
+    for (int j = 0; j < 4; ++j) rb_copy(iss.xs[j] + kt * kRbK, base + j * 1024);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) rb_copy(iss.ws[j] + kt * kRbK, base + kRbOpBytes + j * 1024);
+    for (int j = 0; j < 4; ++j) rb_copy(iss.ws[j] + kt * kRbK, base + kRbOpBytes + j * 1024);
   };
 
-  // Fragments: lane l reads row l%16 of a block at logical chunk l/16 (the
-  // eight k of v_mfma_f32_16x16x32_bf16's A and B operands).
+  // Fragments: for the k half kk of a step, lane l reads row l%16 of a
+  // 16-row block at logical chunk 4 kk + l/16 (the eight k of
+  // v_mfma_f32_16x16x32_bf16's A and B operands).
   const int n16 = lane & 15, g = lane >> 4;
-  const int koff = n16 * 64 + ((g ^ ((n16 >> 1) & 3)) << 4);
+  auto frag_off = [&](int block, int kk) __attribute__((always_inline)) {
+    return (16 * block + n16) * 128 + (((4 * kk + g) ^ ((n16 >> 1) & 7)) << 4);
+  };
   f32x4 acc[8][4];
   auto zero = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -346,16 +345,20 @@ __global__ __launch_bounds__(kRbWaves * 64, 1) void latent_rebuild(ProjectArgs p
   };
   auto compute = [&](int stage) __attribute__((always_inline)) {
     const unsigned char* s = lds + stage * kRbStageBytes;
-    bf16x8 xf[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      xf[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s + (4 * wm + mb) * 1024 + koff));
+    for (int kk = 0; kk < kRbK / 32; ++kk) {
+      bf16x8 xf[4];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const bf16x8 wf =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s + kRbOpBytes + (8 * wn + nb) * 1024 + koff));
+      for (int mb = 0; mb < 4; ++mb)
+        xf[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s + frag_off(4 * wm + mb, kk)));
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[mb], acc[nb][mb], 0, 0, 0);
+      for (int nb = 0; nb < 8; ++nb) {
+        const bf16x8 wf =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(s + kRbOpBytes + frag_off(8 * wn + nb, kk)));
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[mb], acc[nb][mb], 0, 0, 0);
+      }
     }
   };
 
@@ -384,19 +387,14 @@ __global__ __launch_bounds__(kRbWaves * 64, 1) void latent_rebuild(ProjectArgs p
     }
   };
 
-  // Step G: wait for its copies (those of the next two steps, and the stores
-  // of a tile that ended since G's copies were issued, may stay in flight)
-  // and for every wave to finish step G-1, whose stage then takes step G+3.
+  // Step G: wait for its copies (the stores of a tile that ended after they
+  // were issued, at step G-1, may stay in flight) and for every wave to
+  // finish step G-1, whose stage then takes step G+1.
   zero();
-#pragma unroll
-  for (int G = 0; G < kRbStages - 1; ++G)
-    if (G < steps) issue(G);
+  issue(0);
   for (int G = 0; G < steps; ++G) {
-    const int later_copies = kRbCopies * min(2, steps - 1 - G);
-    // A tile ended after step G'' in [G-3, G-1] when G'' % nk == nk - 1: then G % nk < 3, and G >= nk.
-    const int later_stores = (G >= nk && G % nk < kRbStages - 1) ? kRbStores : 0;
-    rb_wait_sync(later_copies + later_stores);
-    if (G + kRbStages - 1 < steps) issue(G + kRbStages - 1);
+    rb_wait_sync(G >= nk && G % nk == 0 ? kRbStores : 0);
+    if (G + 1 < steps) issue(G + 1);
     compute(G % kRbStages);
     if (G % nk == nk - 1) {
       write_tile(tile_of(G / nk).y);
@@ -691,10 +689,9 @@ hipError_t launch_latent_project(const ProjectArgs& p, hipStream_t stream) {
 hipError_t launch_latent_rebuild(const ProjectArgs& p, hipStream_t stream) {
   // Stacked transposed weights of 128 columns per head, two heads per tile;
   // anything else takes the general projection.
-  // The waits assume at least four K steps per tile (one tile end at most
-  // between a step's copies and its use), and y must hold whole 256-row tiles.
+  // y must hold whole 256-row tiles.
   const int64_t padded_rows = ((int64_t)p.rows + kRbM - 1) / kRbM * kRbM;
-  if (!p.w_transposed || p.n_dim != 128 || p.heads % 2 != 0 || p.k_dim % kRbK != 0 || p.k_dim < 4 * kRbK ||
+  if (!p.w_transposed || p.n_dim != 128 || p.heads % 2 != 0 || p.k_dim % kRbK != 0 ||
       p.w_head != (int64_t)p.n_dim * p.k_dim || p.rows < 1 || p.outer < 1 || p.y_head < padded_rows * p.y_row ||
       (int64_t)p.outer * ((p.rows + kRbM - 1) / kRbM) * (p.heads / 2) > INT32_MAX / 2)
     return launch_latent_project(p, stream);
