@@ -324,9 +324,10 @@ kvattn_status kvattn_mla_project(const void* x, const void* w, void* y, int32_t 
  *  workspace    kvattn_mla_explicit_workspace_bytes() bytes, 256-byte aligned:
  *               it holds both weights transposed ([num_heads, 128, d_latent]),
  *               the rebuilt keys (content part) and values,
- *               [batch, num_heads, max_seq_len, 128] bf16 each, for every row
- *               below max_seq_len (the naive form rebuilds them all), then the
- *               split partials.
+ *               [batch, num_heads, R, 128] bf16 each with R = max_seq_len
+ *               rounded up to a multiple of 256 (the naive form rebuilds every
+ *               row below max_seq_len, in tiles of 256 rows; rows from
+ *               max_seq_len on are never read), then the split partials.
  *  Supported: bf16, d_latent 512, d_rope 64, d_head = d_v = 128 (DeepSeek-V2's
  *  shapes).  The rebuilt rows are rounded to bf16 before attention, one more
  *  rounding than the absorbed path takes.
