@@ -195,3 +195,33 @@ def test_full_size_explicit_equals_absorbed_then_up_projected():
     check_explicit(x, out, lse, rows=[0, 31])
     del x
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,h,S", [(2, 16, 300), (3, 8, 68), (1, 6, 520), (2, 32, 1030)])
+def test_rebuilt_rows_match_the_projection(B, h, S):
+    """The rebuilt keys and values the naive form leaves in its workspace, every row below max_seq_len.
+
+    The workspace layout is the one kvattn.h documents: both transposed weights, then the rebuilt keys
+    and values, [B, h, R, 128] bf16 each with R = max_seq_len rounded up to 256.  Each row is
+    c_t W^(i) for the latent row c_t (the fp64 per-head projection of the oracle), whether or not the
+    sequence's length reaches it.
+    """
+    lens = [S] + [max(1, S // (b + 2)) for b in range(1, B)]
+    w = W.MlaWorkload(f"rebuild_{B}_{h}_{S}", B, h, S, 700 + h + S, 1 / np.sqrt(192), form="explicit")
+    note(f"rebuilt rows B={B} h={h} S={S}")
+    x = W.make_mla_explicit_inputs(w, DEV, lens=lens)
+    nbytes = mla_explicit_workspace_bytes(B, h, S)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    mla_explicit_decode(x["q"], x["cache"], x["w_uk"], x["w_uv"], x["seq_lens"], w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    up = lambda v: -(-v // 256) * 256
+    R = up(S)
+    wt = up(h * 512 * 128 * 2)
+    rec = up(B * h * R * 128 * 2)
+    c = f64(x["cache"])[:, :, :512]
+    for name, off, wname in (("keys", 2 * wt, "w_uk"), ("values", 2 * wt + rec, "w_uv")):
+        got = ws[off:off + B * h * R * 128 * 2].view(torch.bfloat16).reshape(B, h, R, 128)[:, :, :S]
+        for b in range(B):
+            rows = np.ascontiguousarray(np.broadcast_to(c[b][:, None, :], (S, h, 512)))
+            ref = oracle.mla_up_project(rows, f64(x[wname]))  # [S, h, 128]
+            assert_close(got[b].float().cpu().numpy().transpose(1, 0, 2), ref, f"{name} b={b}")
