@@ -191,3 +191,50 @@ def test_more_units_than_the_plan_keeps_in_registers():
     np.testing.assert_allclose(got[fin], ref_lse[fin], atol=LSE_ATOL, rtol=1e-4)
     out_g, lse_g = grid_form_call(x, max_len, split, 0, B * h * n_split(w, max_len, split) * (128 * 2 + 4))
     assert torch.equal(out_g, out) and torch.equal(lse_g, lse)
+
+
+@pytest.mark.parametrize("window", [0, 700])
+def test_work_list_holds_each_split_once_full_first_then_longest_first(window):
+    """The device-side work list (16 bytes per slot after the partials, as kvattn.h places it).
+
+    It must hold every split that holds tokens exactly once, as (unit b*g + j, split s, first token, end
+    token) with the one-workgroup-per-split form's boundaries: the full splits first in unit order, then
+    the shorter last splits by length class ceil(32 rest / split), longest first.  A missing split would
+    show in the outputs; a duplicate or a misordered one would not, hence this check.
+    """
+    from decode_attention_kv_03_amd import gqa_workspace_bytes
+
+    B, h, g, S, bs, split = 64, 32, 8, 6000, 16, 64
+    rng = np.random.default_rng(19 + window)
+    lens = lens_with_edges(rng, B, S)
+    w, x, max_len = inputs("work_list", B, h, g, S, "bf16", 83, lens, bs)
+    span = min(max_len, window + 63) if window else max_len
+    nsp = n_split(w, span, split)
+    assert B * g * nsp > PERSISTENT_SLOTS
+    note(f"work list: B={B} g={g} split={split} window={window} splits per unit={nsp}")
+    nbytes = gqa_workspace_bytes(B, h, g, 128, max_len, block_size=bs, split_tokens=split)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    gqa_call(x, split_tokens=split, window=window, workspace=ws)
+    torch.cuda.synchronize()
+    up = lambda v: -(-v // 256) * 256
+    items_off = up(B * h * nsp * (128 * 2 + 4))
+    ctl_off = items_off + up(B * g * nsp * 16)
+    n_items = int(ws[ctl_off:ctl_off + 4].view(torch.int32).item())
+    got = ws[items_off:items_off + 16 * n_items].view(torch.int32).reshape(-1, 4).cpu().numpy()
+
+    full, last = [], []
+    for b in range(B):
+        n = int(min(max(lens[b], 0), max_len))
+        base = (max(0, n - window) if window > 0 and n > window else 0) & ~63
+        f = min((n - base) // split, nsp)
+        for j in range(g):
+            u = b * g + j
+            full += [(u, s, base + s * split, base + (s + 1) * split) for s in range(f)]
+            if f < nsp and n - base - f * split > 0:
+                last.append((u, f, base + f * split, n))
+    assert n_items == len(full) + len(last)
+    assert [tuple(r) for r in got[:len(full)]] == full
+    tail = [tuple(r) for r in got[len(full):]]
+    assert sorted(tail) == sorted(last)
+    classes = [-(-(t1 - t0) * 32 // split) for (_, _, t0, t1) in tail]
+    assert all(a >= b for a, b in zip(classes, classes[1:])), "last splits not longest first"
