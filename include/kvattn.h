@@ -255,7 +255,16 @@ size_t kvattn_gqa_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *  batches keep every compute unit busy; otherwise at most split_tokens
  *  tokens per piece.  Each piece is one workgroup of the decode kernel;
  *  sequences with more than one piece are combined by a log-sum-exp merge.
- *  The plan lives in the workspace, which is therefore never empty.
+ *  The plan lives in the workspace, which is therefore never empty.  With P
+ *  the largest piece count the sizes allow, the workspace holds, each region
+ *  starting at a multiple of 256 bytes: bf16 partial outputs [P, num_heads,
+ *  d_latent], fp32 partial log2-sum-exps [P, num_heads], the pieces int32
+ *  [P][4] = (sequence, first token, end token, 1 if it is its sequence's
+ *  only piece), per sequence int32 [batch][2] = (first piece, piece count;
+ *  an empty sequence keeps one empty piece), then int32 (number of pieces,
+ *  piece length).  A sequence of n tokens cut for piece length t has
+ *  ceil(n / t) pieces of ceil(n / count) tokens rounded up to 32 (the last
+ *  one shorter).
  */
 kvattn_status kvattn_mla_decode(const void* q, const void* cache, const int32_t* block_table,
                                 const int32_t* seq_lens, void* out, float* lse, int32_t batch,

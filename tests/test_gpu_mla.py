@@ -191,3 +191,69 @@ def test_clock_stamps_hook():
     fresh = torch.zeros(4, dtype=torch.int64, device=DEV)
     run(x)
     assert int(fresh.abs().sum()) == 0
+
+
+def _pieces_of(n, t):
+    return -(-n // t) if n > 0 else 1
+
+
+@pytest.mark.parametrize("B,seed,max_len,split,bs", [
+    (40, 11, 3000, 0, 0),
+    (40, 12, 3000, 0, 32),     # paged
+    (600, 13, 1500, 0, 0),     # more sequences than the plan keeps in registers, more than 256 pieces
+    (7, 14, 9000, 0, 0),       # few sequences: many pieces each
+    (9, 15, 5000, 320, 0),     # a requested piece length
+])
+def test_device_plan_matches_its_definition(B, seed, max_len, split, bs):
+    """The plan the device leaves in the workspace (laid out as kvattn.h documents it).
+
+    With split_tokens 0 the piece length t is the shortest multiple of 32, at least 256, that cuts the
+    batch into at most max(256, B) pieces (an empty sequence keeps one empty piece); otherwise t is
+    split_tokens.  A sequence of n tokens has ceil(n / t) consecutive pieces of ceil(n / count) tokens
+    rounded up to 32, the last one shorter, flagged when a sequence has only one.  Results only show a
+    plan that loses or doubles tokens; a longer t than needed, or pieces out of order, would not.
+    """
+    from decode_attention_kv_03_amd import mla_workspace_bytes
+
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, max_len + 1, size=B).astype(np.int32)
+    lens[0], lens[-1] = 0, 1
+    h = 16
+    w = W.MlaWorkload(f"mla_plan_def_{B}", B, h, max_len, 950 + seed, 1 / np.sqrt(192), block_size=bs)
+    x = W.make_mla_inputs(w, DEV, lens=lens)
+    len_cap = x["block_table"].shape[1] * bs if bs else max_len
+    note(f"mla plan definition B={B} max_len={max_len} split={split} block_size={bs}")
+    nbytes = mla_workspace_bytes(B, h, len_cap, block_size=bs, split_tokens=split)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    mla_decode(x["q"], x["cache"], x["seq_lens"], w.scale, block_table=x["block_table"], split_tokens=split,
+               workspace=ws)
+    torch.cuda.synchronize()
+
+    up = lambda v: -(-v // 256) * 256
+    P = max(256, B) if split == 0 else B * -(-len_cap // split)
+    o_pieces = up(P * h * 512 * 2) + up(P * h * 4)
+    o_seq = o_pieces + up(P * 16)
+    o_count = o_seq + up(B * 8)
+    host = ws.cpu()
+    n_pieces, t = (int(v) for v in host[o_count:o_count + 8].view(torch.int32))
+    seq = host[o_seq:o_seq + 8 * B].view(torch.int32).reshape(B, 2).numpy()
+    pieces = host[o_pieces:o_pieces + 16 * n_pieces].view(torch.int32).reshape(-1, 4).numpy()
+
+    n = [int(v) for v in lens]
+    if split == 0:
+        cap = max(256, B)
+        assert t % 32 == 0 and t >= 256
+        assert sum(_pieces_of(v, t) for v in n) <= cap
+        assert t == 256 or sum(_pieces_of(v, t - 32) for v in n) > cap, "a shorter piece length fits"
+    else:
+        assert t == split
+    first = 0
+    for b, v in enumerate(n):
+        count = _pieces_of(v, t)
+        assert tuple(seq[b]) == (first, count), b
+        plen = (-(-v // count) + 31) // 32 * 32 if v > 0 else 0
+        for j in range(count):
+            lo = j * plen
+            assert tuple(pieces[first + j]) == (b, lo, min(lo + plen, v), int(count == 1)), (b, j)
+        first += count
+    assert n_pieces == first
