@@ -25,12 +25,13 @@
 // into a four-stage LDS ring with global_load_lds_dwordx4 carrying the
 // non-temporal hint (no register staging); each wave issues nine of a tile's
 // 36 copy instructions, spread over its score products.  In LDS a tile is
-// stored as 36 blocks of 1 KiB, [row half (16 rows)][slab of 4 chunks
-// (64 bytes of each row)], one per copy instruction, with the four 16-byte
-// chunks of row r XOR-swizzled by swz(r % 16).  Score reads then take one
-// whole 1 KiB block per instruction, and the transposing reads of the value
-// product (ds_read_b64_tr_b16: 4 consecutive rows x 16 columns per 16-lane
-// group) spread over all banks.  The copies are issued as inline assembly
+// stored as 36 blocks of 1 KiB, [row group (8 rows)][segment (128 bytes of
+// each row)], one per copy instruction, so that every copy fetches whole
+// 128-byte cache lines (with 16 rows x 64 bytes per instruction, each line
+// was requested in two halves); the eight 16-byte chunks of row r are
+// XOR-swizzled by swz(r % 16).  Score reads (16 rows x 64 bytes) and the
+// transposing reads of the value product (ds_read_b64_tr_b16: 4 consecutive
+// rows x 16 columns per 16-lane group) then spread over all banks.  The copies are issued as inline assembly
 // and awaited with explicit vmcnt counts followed by a bare s_barrier; a
 // full workgroup fence, or the compiler's own alias-based waits, would
 // drain every tile in flight.
@@ -80,14 +81,13 @@ constexpr int kVDepth = 6;                     // ... and value product
 constexpr int kStgPitch = 2 * kMlaLatent + 32; // epilogue staging: bytes per head row
 static_assert(kWaves * 32 * kStgPitch <= kNBuf * kTileBytes, "staging fits in the tile ring");
 
-// Chunk swizzle of tile row r (r % 16 = rr): the physical chunk is the
-// logical one XOR (rr / 2) % 4.  Any swizzle keeps the 1 KiB copies and
-// score reads free of bank conflicts (each touches one whole block); for the
-// transposing reads, where lane group g takes rows 4g..4g+3 at the same
-// logical chunks, this one measured the fewest bank-conflict stall cycles
-// of the XOR swizzles tried (8 % of LDS-busy cycles, against 37-51 % for
-// swizzles on rr % 4, rr / 4 or none).
-__device__ __forceinline__ int swz(int rr) { return (rr >> 1) & 3; }
+// Chunk swizzle of tile row r (r % 16 = rr), 128-byte rows of a segment:
+// the physical chunk (0 .. 7) is the logical one XOR 2 ((rr / 2) % 4) +
+// (rr / 8).  A score read's 16 lanes (rows rr = 0 .. 15 at one logical
+// chunk) then fall on 16 distinct 16-byte bank slots, and a transposing
+// read's 32 lanes (rows 4g .. 4g+7, two adjacent chunks) on 32 distinct
+// 8-byte ones.
+__device__ __forceinline__ int swz(int rr) { return (((rr >> 1) & 3) << 1) | ((rr >> 3) & 1); }
 
 // Block-table index and in-block slot of token t (paged cache).
 __device__ __forceinline__ int block_of(const DecodeArgs& a, int t) {
@@ -129,26 +129,26 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 
   const uint16_t* cbase = static_cast<const uint16_t*>(a.k);
   // Copies of one tile: 36 wave instructions, nine from each wave.
-  // Instruction `inst` fills LDS block inst: rows 16*(inst/18) + lane/4 of
-  // the tile, slab inst%18; lane l lands at physical chunk l%4 of its row's
-  // slab, which holds logical chunk 4*slab + ((l%4) ^ swz(l/4)).  Wave w's
-  // instructions 9w .. 9w+8 lie in one 16-row half.
+  // Instruction `inst` fills LDS block inst: row group inst/9 (rows 8*(inst/9)
+  // + lane/8 of the tile), segment inst%9; lane l lands at physical chunk l%8
+  // of its row's segment, which holds logical chunk 8*segment + ((l%8) ^
+  // swz(row)).  Wave w's instructions 9w .. 9w+8 fill row group w.
   const int inst0 = wave * kDmaPer;
-  const int drow = lane >> 2, dchunk = (lane & 3) ^ swz(drow);
-  // Byte offset of the lane's source inside a 16-row run of cache rows (slab 0).
+  const int drow = lane >> 3, dchunk = (lane & 7) ^ swz(8 * wave + drow);
+  // Byte offset of the lane's source inside an 8-row run of cache rows (segment 0).
   const uint32_t doff = (uint32_t)((drow * kRowElems + dchunk * 8) * 2);
   // Contiguous rows of this sequence start here; a paged cache looks each row up.
   const uint16_t* seq_base = cbase + (a.block_size == 0 ? (int64_t)b * a.cache_len * kRowElems : 0);
   const int32_t* tbl = a.block_table + (int64_t)b * a.max_blocks;
-  // Fast copies need each 16-row half of the tile to be one run of
+  // Fast copies need each 8-row group of the tile to be one run of
   // consecutive cache rows: always true for a contiguous cache, and for a
-  // paged one whose block size is a multiple of 16 (tiles start at
-  // multiples of 32 tokens).  The ragged last tile of a piece takes the
-  // general path, which clamps every row into the piece.
-  const bool halves_contiguous = a.block_size == 0 || (a.block_size & 15) == 0;
-  // First cache row of the 16-row run starting at token t (a multiple of 16;
+  // paged one whose block size is a multiple of 8 (tiles start at multiples
+  // of 32 tokens).  The ragged last tile of a piece takes the general path,
+  // which clamps every row into the piece.
+  const bool groups_contiguous = a.block_size == 0 || (a.block_size & 7) == 0;
+  // First cache row of the 8-row run starting at token t (a multiple of 8;
   // fast path only).  A paged lookup is a scalar table load.
-  auto half_base = [&](int t) __attribute__((always_inline)) -> const uint16_t* {
+  auto group_base = [&](int t) __attribute__((always_inline)) -> const uint16_t* {
     if (a.block_size == 0) return seq_base + (int64_t)t * kRowElems;
     const int32_t* ep = tbl + block_of(a, t);
     int e;
@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
 #pragma unroll 1
     for (int u = 0; u < kDmaPer; ++u) {
       const int inst = inst0 + u;
-      const int t = min(t0 + 16 * (inst / 18) + drow, t_end - 1);
-      const int chunk = 4 * (inst % 18) + dchunk;
+      const int t = min(t0 + 8 * wave + drow, t_end - 1);
+      const int chunk = 8 * u + dchunk;
       int64_t off;
       if (a.block_size == 0) {
         off = (int64_t)t * kRowElems;
@@ -180,14 +180,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
     }
   };
   auto fast_tile = [&](int t0) __attribute__((always_inline)) {
-    return halves_contiguous && t0 + kT <= t_end;
+    return groups_contiguous && t0 + kT <= t_end;
   };
   auto issue_tile = [&](int t0, int buf) __attribute__((always_inline)) {
     if (fast_tile(t0)) {
-      const uint16_t* hb = half_base(t0 + 16 * (inst0 / 18));
+      const uint16_t* gb = group_base(t0 + 8 * wave);
       const uint32_t dst = (uint32_t)(uintptr_t)&tiles[buf][0] + inst0 * 1024;
 #pragma unroll
-      for (int u = 0; u < kDmaPer; ++u) dma16s(doff, hb + (inst0 % 18 + u) * 32, dst + u * 1024);
+      for (int u = 0; u < kDmaPer; ++u) dma16s(doff, gb + u * 64, dst + u * 1024);
     } else {
       issue_tile_general(t0, buf);
     }
@@ -234,21 +234,26 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
   // Per-lane LDS byte offsets inside a tile.
-  // Scores (A operand): lane l reads row 16*tb + l%16 at logical chunk
-  // 4*ks + l/16 (slab ks): the offset below plus an immediate
-  // kHalfBytes * tb + 1024 * ks.
-  const int koff = n16 * 64 + ((g ^ swz(n16)) << 4);
+  // Scores (A operand): lane l reads row 16*tb + l%16 (row group 2*tb +
+  // l%16/8) at logical chunk 4*ks + l/16 (segment ks/2, chunk 4*(ks%2) +
+  // l/16 within it): one of the two offsets below, by ks's parity, plus an
+  // immediate kHalfBytes * tb + 1024 * (ks/2).
+  const int kbase = (n16 >> 3) * 9 * 1024 + (n16 & 7) * 128;
+  const int koff_even = kbase + ((g ^ swz(n16)) << 4);
+  const int koff_odd = kbase + (((4 + g) ^ swz(n16)) << 4);
   // Values (A operand): lane l needs column 16*cb + l%16 at the tokens
   // 4g..4g+3 (first read) and 16+4g..16+4g+3 (second read), g = l/16.  The
   // transposing read returns to lane n of a 16-lane group element n%4 of the
   // 4-element piece addressed by lane 4v + n/4, for rows v = 0..3; so lane n
   // addresses row 4g + n/4 and the four columns 16*cb + 4*(n%4) .. +3
   // (logical chunk 2*cb + (n%4)/2, byte 8*(n%2)), and receives column
-  // 16*cb + n.  The slab cb/2 is an immediate 1024 * (cb/2); the chunk
-  // within the slab depends on cb's parity, hence two base offsets.
+  // 16*cb + n.  The segment cb/4 is an immediate 1024 * (cb/4); the chunk
+  // within the segment depends on cb % 4, hence four base offsets.
   const int vrr = 4 * g + (n16 >> 2);
-  const int voff_even = vrr * 64 + ((((n16 & 3) >> 1) ^ swz(vrr)) << 4) + 8 * (n16 & 1);
-  const int voff_odd = vrr * 64 + (((2 + ((n16 & 3) >> 1)) ^ swz(vrr)) << 4) + 8 * (n16 & 1);
+  const int vbase = (vrr >> 3) * 9 * 1024 + (vrr & 7) * 128 + 8 * (n16 & 1);
+  int voff[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) voff[m] = vbase + (((2 * m + ((n16 & 3) >> 1)) ^ swz(vrr)) << 4);
 
   const float c = a.scale_log2;
   const float neutral = c >= 0.f ? -INFINITY : INFINITY;
@@ -278,7 +283,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
     // Read j: token half tb = j % 2, reduction step ks = j / 2.
     auto read_k = [&](int j) __attribute__((always_inline)) {
       return __builtin_bit_cast(bf16x8,
-                                *reinterpret_cast<const u32x4*>(tile + koff + kHalfBytes * (j & 1) + 1024 * (j >> 1)));
+                                *reinterpret_cast<const u32x4*>(tile + (((j >> 1) & 1) ? koff_odd : koff_even) +
+                                                                kHalfBytes * (j & 1) + 1024 * (j >> 2)));
     };
     bf16x8 ka[kKDepth];
 #pragma unroll
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
   auto values = [&](int it, const bf16x8 (&pp)[2], auto between) __attribute__((always_inline)) {
     const auto* tile_lds = (const __attribute__((address_space(3))) unsigned char*)tiles[it % kNBuf];
     auto read_v = [&](int cb) __attribute__((always_inline)) {
-      const int off = ((cb & 1) ? voff_odd : voff_even) + 1024 * (cb >> 1);
+      const int off = voff[cb & 3] + 1024 * (cb >> 2);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_lds + off));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile_lds + off + kHalfBytes));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -430,10 +436,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void mla_split_bf16(DecodeArgs a) {
     const int tn = t_begin + (it + 2) * kT;
     f32x4 s[2][2];
     if (it + 2 < n_tiles && fast_tile(tn)) {
-      const uint16_t* hb = half_base(tn + 16 * (inst0 / 18));
+      const uint16_t* gb = group_base(tn + 8 * wave);
       const uint32_t dst = (uint32_t)(uintptr_t)&tiles[(it + 2) % kNBuf][0] + inst0 * 1024;
-      const int slab0 = inst0 % 18;
-      scores(it, s, [&](int u) __attribute__((always_inline)) { dma16s(doff, hb + (slab0 + u) * 32, dst + u * 1024); });
+      scores(it, s, [&](int u) __attribute__((always_inline)) { dma16s(doff, gb + u * 64, dst + u * 1024); });
     } else {
       if (it + 2 < n_tiles) issue_tile_general(tn, (it + 2) % kNBuf);
       scores(it, s, [](int) {});

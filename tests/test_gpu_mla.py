@@ -125,7 +125,7 @@ def test_device_plan_ragged_batches(B, lens_seed, max_len, split, bs):
     np.testing.assert_allclose(got[fin], l_ref[fin], atol=LSE_ATOL, rtol=1e-4)
 
 
-@pytest.mark.parametrize("bs", [16, 5, 64])
+@pytest.mark.parametrize("bs", [16, 5, 64, 8, 24])
 def test_paged(bs):
     w = W.MlaWorkload(f"mla_paged_bs{bs}", 4, 128, 400, 40 + bs, 1 / np.sqrt(192), block_size=bs)
     note(f"mla paged bs={bs}")
