@@ -82,12 +82,12 @@ constexpr int kStgPitch = 2 * kMlaLatent + 32; // epilogue staging: bytes per he
 static_assert(kWaves * 32 * kStgPitch <= kNBuf * kTileBytes, "staging fits in the tile ring");
 
 // Chunk swizzle of tile row r (r % 16 = rr), 128-byte rows of a segment:
-// the physical chunk (0 .. 7) is the logical one XOR 2 ((rr / 2) % 4) +
-// (rr / 8).  A score read's 16 lanes (rows rr = 0 .. 15 at one logical
-// chunk) then fall on 16 distinct 16-byte bank slots, and a transposing
-// read's 32 lanes (rows 4g .. 4g+7, two adjacent chunks) on 32 distinct
-// 8-byte ones.
-__device__ __forceinline__ int swz(int rr) { return (((rr >> 1) & 3) << 1) | ((rr >> 3) & 1); }
+// the physical chunk (0 .. 7) is the logical one XOR rr % 8.  Of the
+// swizzles measured in the kernel (LDS bank-conflict stall cycles over
+// LDS-busy cycles), this one gave 8 %, against 35-51 % for XORs with
+// (rr / 2) % 8, 2 ((rr / 2) % 4) + rr / 8 and other mixes of the row bits,
+// and 75 % for none, whose kernel ran a fifth slower.
+__device__ __forceinline__ int swz(int rr) { return rr & 7; }
 
 // Block-table index and in-block slot of token t (paged cache).
 __device__ __forceinline__ int block_of(const DecodeArgs& a, int t) {
