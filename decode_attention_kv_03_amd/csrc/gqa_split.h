@@ -10,9 +10,11 @@
 // Work decomposition.  One workgroup (4 waves) owns one (sequence, KV head,
 // split) and walks the split's tokens in tiles of 16 KiB per tensor (64
 // bf16 rows of 256 B, or 128 fp8 rows of 128 B):
-//  * the 1-D grid is XCD-aware: workgroup w runs on XCD w % 8, and all splits
-//    of one (sequence, KV head) share that residue, so the group's queries
-//    are fetched into one XCD's L2;
+//  * the 1-D grid is XCD-aware: workgroup w runs on XCD w % 8, and when the
+//    (sequence, KV head) units divide evenly among the eight XCDs all splits
+//    of a unit share that residue, so the group's queries are fetched into
+//    one XCD's L2; otherwise (a single long sequence, say) consecutive
+//    workgroups take consecutive splits, so that every XCD gets work;
 //  * tiles stream from HBM straight into a two-stage LDS ring with
 //    global_load_lds_dwordx4 carrying the non-temporal hint (the cache is
 //    read once per step); one tile is in flight while the other is consumed.
@@ -73,10 +75,17 @@ struct GqaWork {
 // Decode the workgroup's work item; false if the workgroup has nothing to do.
 template <int kTile>
 __device__ __forceinline__ bool gqa_work(const DecodeArgs& a, GqaWork& w) {
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  w.split = slot % a.n_split;
-  const int unit = (slot / a.n_split) * 8 + xcd;
-  if (unit >= a.batch * a.num_kv_heads) return false;
+  const int units = a.batch * a.num_kv_heads;
+  int unit;
+  if ((units & 7) == 0) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    w.split = slot % a.n_split;
+    unit = (slot / a.n_split) * 8 + xcd;
+  } else {
+    w.split = blockIdx.x % a.n_split;
+    unit = blockIdx.x / a.n_split;
+  }
+  if (unit >= units) return false;
   w.b = unit / a.num_kv_heads;
   w.j = unit - w.b * a.num_kv_heads;
   const int len = clamp_len(a.seq_lens[w.b], a.len_cap);
