@@ -6,10 +6,15 @@
 // scaled scores).  The exact result over all tokens is
 //     M = max_s lse_s,  w_s = 2^(lse_s - M),  o = sum_s w_s o_s / sum_s w_s,
 //     lse = M + log2(sum_s w_s)
-// (softmax over a union of token sets).  One wave per (sequence, head).
+// (softmax over a union of token sets).  One workgroup per (sequence, head),
+// of one wave, or of up to eight when a row has many splits (a long
+// sequence): every wave then finds M and the normaliser over all splits
+// itself (a few loads per lane), sums the weighted partials of its share of
+// the splits, and the waves' sums are added through LDS.
 // The splits of a bf16-output call (bf16 or fp8 cache) hand over bf16
 // partial outputs, those of an fp32 call fp32 ones; log-sum-exps and the
 // combination are fp32 throughout.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -23,7 +28,7 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <int DV, bool BF16>
-__global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
+__global__ __launch_bounds__(512) void lse_merge(DecodeArgs a) {
   // Lane l handles float4 columns c = l % kRowLanes (+ kRowLanes * k) of
   // the splits s = l / kRowLanes + kSplitGroups * u.  Every load of a round
   // (the splits' log-sum-exps and partial outputs) is issued before any is
@@ -34,7 +39,8 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
   constexpr int kSplitGroups = 64 / kRowLanes;        // splits read side by side
   constexpr int kCols = kVec / kRowLanes;             // float4 columns per lane
   constexpr int kU = 8;                               // splits per lane and round
-  const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
   const int c = lane % kRowLanes, sg = lane / kRowLanes;
   const int len = clamp_len(a.seq_lens[b], a.len_cap);
   int nv = (len - window_base(len, a.window) + a.split_tokens - 1) / a.split_tokens;
@@ -64,7 +70,8 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
         x[u][k] = *reinterpret_cast<const Raw*>(po + (int64_t)s * DV + 4 * (c + kRowLanes * k));
     }
   };
-  if (nv > 0) load_round(0);  // in flight while the maximum and the normaliser are found
+  constexpr int kRound = kSplitGroups * kU;  // splits per round of one wave; wave w takes rounds w, w + n_waves, ...
+  if (nv > wave * kRound) load_round(wave * kRound);  // in flight while the maximum and the normaliser are found
 
   // Lane l keeps the log-sum-exp of split l; splits past 64 are reread.
   const float lv = lane < nv ? pl[lane] : -INFINITY;
@@ -84,8 +91,8 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < kCols; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (!empty) {
-    for (int s0 = 0; s0 < nv; s0 += kSplitGroups * kU) {
-      if (s0 > 0) load_round(s0);
+    for (int s0 = wave * kRound; s0 < nv; s0 += n_waves * kRound) {
+      if (s0 > wave * kRound) load_round(s0);
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const float w = s0 + sg + kSplitGroups * u < nv ? fast_exp2(ls[u] - M) : 0.f;
@@ -101,6 +108,19 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
     for (int k = 0; k < kCols; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[k][e] += __shfl_xor(acc[k][e], m, 64);
+  if (n_waves > 1) {
+    // The other waves' sums, added by wave 0.
+    __shared__ f32x4 red[7][kRowLanes * kCols];
+    if (wave > 0 && sg == 0) {
+#pragma unroll
+      for (int k = 0; k < kCols; ++k) red[wave - 1][c + kRowLanes * k] = acc[k];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int w2 = 1; w2 < n_waves; ++w2)
+#pragma unroll
+      for (int k = 0; k < kCols; ++k) acc[k] += red[w2 - 1][c + kRowLanes * k];
+  }
   if (sg == 0) {
 #pragma unroll
     for (int k = 0; k < kCols; ++k) {
@@ -121,7 +141,8 @@ __global__ __launch_bounds__(64) void lse_merge(DecodeArgs a) {
 
 hipError_t launch_merge(const DecodeArgs& a, bool out_bf16, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.batch);
-  const dim3 block(64);
+  // One wave per row, or one per 32 splits (two rounds of loads each) up to eight.
+  const dim3 block(64 * std::min(8, std::max(1, (a.n_split + 31) / 32)));
   if (out_bf16) lse_merge<kHeadDim, true><<<grid, block, 0, stream>>>(a);
   else lse_merge<kHeadDim, false><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();

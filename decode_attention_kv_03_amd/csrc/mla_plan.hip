@@ -17,6 +17,8 @@
 // split_tokens fixes t instead.  A sequence covered by one piece gets its
 // output written directly by the decode kernel; the others are combined by
 // the log-sum-exp merge below.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kvattn_internal.h"
 
@@ -32,6 +34,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // The plan runs as one wave: lane l handles sequences l, l+64, ...; the
 // lengths of the first kCached rounds stay in registers across the search.
 constexpr int kCached = 8;
+
+// Most waves in one workgroup of the piece merge.
+constexpr int kMergeMaxWaves = 16;
 
 __device__ __forceinline__ int64_t align32(int64_t x) { return (x + 31) & ~int64_t(31); }
 
@@ -132,7 +137,11 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
   }
 
   // Sequences in rounds of 64; the first piece of each is an exclusive
-  // prefix sum carried across rounds.
+  // prefix sum carried across rounds.  The pieces of a round are written by
+  // the whole wave, piece q by lane q mod 64, which finds its sequence by a
+  // binary search over the round's inclusive piece counts (a long sequence
+  // has hundreds of pieces).
+  __shared__ int s_incl[64], s_len[64];
   int carry = 0;
   for (int base = 0, i = 0; base < p.batch; base += 64, ++i) {
     const int b = base + lane;
@@ -143,17 +152,29 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
     if (i >= kCached && b < p.batch) len = clamp_len(p.seq_lens[b], p.len_cap);
     const int count = b < p.batch ? pieces_of(len, t) : 0;
     const int incl = wave_scan_int(count);
-    const int first = carry + incl - count;
-    if (b < p.batch) {
-      p.seq_pieces[b] = make_int2(first, count);
-      const int64_t plen = len > 0 ? piece_len(len, t) : 0;
-      for (int j = 0; j < count; ++j) {
-        const int64_t lo = j * plen;
-        const int64_t hi = lo + plen < len ? lo + plen : len;
-        p.pieces[first + j] = make_int4(b, (int)lo, (int)hi, count == 1 ? 1 : 0);
+    if (b < p.batch) p.seq_pieces[b] = make_int2(carry + incl - count, count);
+    s_incl[lane] = incl;
+    s_len[lane] = len;
+    __syncthreads();
+    const int round_total = __shfl(incl, 63, 64);
+    for (int q = lane; q < round_total; q += 64) {
+      // First k with s_incl[k] > q: the sequence holding piece q (sequences
+      // with no pieces have s_incl[k] == s_incl[k - 1] and are skipped).
+      int lo_k = 0, hi_k = 63;
+      while (lo_k < hi_k) {
+        const int mid = (lo_k + hi_k) >> 1;
+        if (s_incl[mid] > q) hi_k = mid;
+        else lo_k = mid + 1;
       }
+      const int before = lo_k > 0 ? s_incl[lo_k - 1] : 0;
+      const int cnt = s_incl[lo_k] - before, sl = s_len[lo_k], j = q - before;
+      const int64_t plen = sl > 0 ? piece_len(sl, t) : 0;
+      const int64_t lo = j * plen;
+      const int64_t hi = lo + plen < sl ? lo + plen : sl;
+      p.pieces[carry + q] = make_int4(base + lo_k, (int)lo, (int)hi, cnt == 1 ? 1 : 0);
     }
-    carry += __shfl(incl, 63, 64);
+    __syncthreads();  // the next round rewrites s_incl and s_len
+    carry += round_total;
   }
   if (lane == 0) {
     p.plan_count[0] = carry;
@@ -164,45 +185,82 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
 // Log-sum-exp merge of the pieces of each sequence with more than one.
 // Piece q leaves o_q (normalised over its own tokens, rounded to bf16) and
 // lse_q (fp32, log2 of its normaliser); M = max lse_q, w_q = 2^(lse_q - M), o = sum w_q o_q / sum w_q,
-// lse = M + log2 sum w_q.  One wave per (sequence, head).
-__global__ __launch_bounds__(64) void mla_merge_pieces(DecodeArgs a) {
-  const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+// lse = M + log2 sum w_q.  One workgroup per (sequence, head): one wave, or
+// up to sixteen when sequences have many pieces (a long one): every wave then
+// finds M and the normaliser over all pieces itself, sums the weighted
+// partials of its share of the pieces, and the waves' sums are added
+// through LDS.
+__global__ __launch_bounds__(1024) void mla_merge_pieces(DecodeArgs a) {
+  const int head = blockIdx.x, b = blockIdx.y, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
   const int2 sp = a.seq_pieces[b];
-  if (sp.y <= 1) return;  // written directly by the decode kernel
+  const int n = sp.y;
+  if (n <= 1) return;  // written directly by the decode kernel
   const int h = a.num_q_heads;
   const int64_t row = (int64_t)b * h + head;
+  const float* pl = a.part_lse + (int64_t)sp.x * h + head;  // piece s: pl[s * h]
 
-  float M = -INFINITY;
-  for (int s = lane; s < sp.y; s += 64) M = fmaxf(M, a.part_lse[(int64_t)(sp.x + s) * h + head]);
+  // Partial outputs are bf16 [piece, head, 512].  Lane l owns columns 8l ..
+  // 8l+7 (one 16-byte load per piece); a round takes eight pieces, all of
+  // whose loads are issued before any is used, and wave w takes rounds w,
+  // w + n_waves, ...  The wave's first round is in flight while the maximum
+  // and the normaliser are found.
+  const uint16_t* po = reinterpret_cast<const uint16_t*>(a.part_o) + ((int64_t)sp.x * h + head) * kMlaLatent + 8 * lane;
+  u32x4 x[8];
+  float ls[8];
+  auto load_round = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, n - 1);  // past the last piece: reread it with weight 0
+      ls[u] = pl[(int64_t)s * h];
+      x[u] = *reinterpret_cast<const u32x4*>(po + (int64_t)s * h * kMlaLatent);
+    }
+  };
+  if (n > 8 * wave) load_round(8 * wave);
+
+  // Lane l keeps the log-sum-exps of pieces l, l + 64, l + 128, l + 192;
+  // pieces past 256 are reread.
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lv[i] = lane + 64 * i < n ? pl[(int64_t)(lane + 64 * i) * h] : -INFINITY;
+  float M = fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3]));
+  for (int s = lane + 256; s < n; s += 64) M = fmaxf(M, pl[(int64_t)s * h]);
   M = wave_reduce_max(M);
   float L = 0.f;
-  if (M != -INFINITY)
-    for (int s = lane; s < sp.y; s += 64) L += fast_exp2(a.part_lse[(int64_t)(sp.x + s) * h + head] - M);
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L += fast_exp2(lv[i] - M);  // 2^-inf = 0 past the end
+    for (int s = lane + 256; s < n; s += 64) L += fast_exp2(pl[(int64_t)s * h] - M);
+  }
   L = wave_reduce_sum(L);
   const bool empty = !(L > 0.f);
   const float inv = empty ? 0.f : 1.f / L;
 
-  // Partial outputs are bf16 [piece, head, 512].  Lane l owns columns 8l ..
-  // 8l+7 (one 16-byte load per piece); pieces are taken eight at a time so
-  // eight loads per lane are in flight.
-  const uint16_t* po = reinterpret_cast<const uint16_t*>(a.part_o);
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
   if (!empty) {
-    for (int s0 = 0; s0 < sp.y; s0 += 8) {
-      u32x4 x[8];
-      float w[8];
+    for (int s0 = 8 * wave; s0 < n; s0 += 8 * n_waves) {
+      if (s0 > 8 * wave) load_round(s0);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int s = min(s0 + u, sp.y - 1);  // past the last piece: reread it with weight 0
-        const int64_t pr = (int64_t)(sp.x + s) * h + head;
-        w[u] = s0 + u < sp.y ? fast_exp2(a.part_lse[pr] - M) : 0.f;
-        x[u] = *reinterpret_cast<const u32x4*>(po + pr * kMlaLatent + 8 * lane);
+        const float w = s0 + u < n ? fast_exp2(ls[u] - M) : 0.f;
+        acc0 += w * f32x4{bf16_lo(x[u][0]), bf16_hi(x[u][0]), bf16_lo(x[u][1]), bf16_hi(x[u][1])};
+        acc1 += w * f32x4{bf16_lo(x[u][2]), bf16_hi(x[u][2]), bf16_lo(x[u][3]), bf16_hi(x[u][3])};
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc0 += w[u] * f32x4{bf16_lo(x[u][0]), bf16_hi(x[u][0]), bf16_lo(x[u][1]), bf16_hi(x[u][1])};
-        acc1 += w[u] * f32x4{bf16_lo(x[u][2]), bf16_hi(x[u][2]), bf16_lo(x[u][3]), bf16_hi(x[u][3])};
-      }
+    }
+  }
+  if (n_waves > 1) {
+    // The other waves' sums, added by wave 0 (the launch sizes the LDS:
+    // 2 x 64 float4 per wave past the first, none for a one-wave row).
+    extern __shared__ f32x4 red[];
+    if (wave > 0) {
+      red[(wave - 1) * 128 + lane] = acc0;
+      red[(wave - 1) * 128 + 64 + lane] = acc1;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    for (int w2 = 1; w2 < n_waves; ++w2) {
+      acc0 += red[(w2 - 1) * 128 + lane];
+      acc1 += red[(w2 - 1) * 128 + 64 + lane];
     }
   }
   acc0 *= inv;
@@ -222,7 +280,11 @@ hipError_t launch_mla_plan(const MlaPlanArgs& p, hipStream_t stream) {
 
 hipError_t launch_mla_merge_pieces(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.batch);
-  mla_merge_pieces<<<grid, 64, 0, stream>>>(a);
+  // One wave per row, or, when the plan may give a sequence many pieces, one
+  // per 16 of them (two rounds of loads each) up to kMergeMaxWaves.
+  const int per_seq = (a.max_pieces + a.batch - 1) / a.batch;
+  const int waves = per_seq > 16 ? std::min(kMergeMaxWaves, (per_seq + 15) / 16) : 1;
+  mla_merge_pieces<<<grid, 64 * waves, (waves - 1) * 128 * sizeof(f32x4), stream>>>(a);
   return hipGetLastError();
 }
 

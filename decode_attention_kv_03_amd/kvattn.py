@@ -207,7 +207,7 @@ def _workspace(nbytes, workspace, device):
     if nbytes == 0:
         return None
     if workspace is None:
-        return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)  # the library needs no initialised contents
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"kvattn: workspace needs {nbytes} bytes")
     return workspace
