@@ -73,6 +73,12 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ int wave_scan_int(int v) {
   const int lane = threadIdx.x;
@@ -137,10 +143,12 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
   }
 
   // Sequences in rounds of 64; the first piece of each is an exclusive
-  // prefix sum carried across rounds.  The pieces of a round are written by
-  // the whole wave, piece q by lane q mod 64, which finds its sequence by a
-  // binary search over the round's inclusive piece counts (a long sequence
-  // has hundreds of pieces).
+  // prefix sum carried across rounds.  When no sequence of a round has more
+  // than kOwnPieces pieces, each lane writes its own sequence's pieces;
+  // otherwise (a long sequence has hundreds) the whole wave writes them,
+  // piece q by lane q mod 64, which finds its sequence by a binary search
+  // over the round's inclusive piece counts.
+  constexpr int kOwnPieces = 16;
   __shared__ int s_incl[64], s_len[64];
   int carry = 0;
   for (int base = 0, i = 0; base < p.batch; base += 64, ++i) {
@@ -152,11 +160,22 @@ __global__ __launch_bounds__(64) void mla_plan(MlaPlanArgs p) {
     if (i >= kCached && b < p.batch) len = clamp_len(p.seq_lens[b], p.len_cap);
     const int count = b < p.batch ? pieces_of(len, t) : 0;
     const int incl = wave_scan_int(count);
-    if (b < p.batch) p.seq_pieces[b] = make_int2(carry + incl - count, count);
+    const int round_total = __shfl(incl, 63, 64);
+    const int first = carry + incl - count;
+    if (b < p.batch) p.seq_pieces[b] = make_int2(first, count);
+    if (wave_max_int(count) <= kOwnPieces) {
+      const int64_t plen = len > 0 ? piece_len(len, t) : 0;
+      for (int j = 0; j < count; ++j) {
+        const int64_t lo = j * plen;
+        const int64_t hi = lo + plen < len ? lo + plen : len;
+        p.pieces[first + j] = make_int4(b, (int)lo, (int)hi, count == 1 ? 1 : 0);
+      }
+      carry += round_total;
+      continue;
+    }
     s_incl[lane] = incl;
     s_len[lane] = len;
     __syncthreads();
-    const int round_total = __shfl(incl, 63, 64);
     for (int q = lane; q < round_total; q += 64) {
       // First k with s_incl[k] > q: the sequence holding piece q (sequences
       // with no pieces have s_incl[k] == s_incl[k - 1] and are skipped).

@@ -197,14 +197,15 @@ def _pieces_of(n, t):
     return -(-n // t) if n > 0 else 1
 
 
-@pytest.mark.parametrize("B,seed,max_len,split,bs", [
-    (40, 11, 3000, 0, 0),
-    (40, 12, 3000, 0, 32),     # paged
-    (600, 13, 1500, 0, 0),     # more sequences than the plan keeps in registers, more than 256 pieces
-    (7, 14, 9000, 0, 0),       # few sequences: many pieces each
-    (9, 15, 5000, 320, 0),     # a requested piece length
+@pytest.mark.parametrize("B,seed,max_len,split,bs,mixed", [
+    (40, 11, 3000, 0, 0, False),
+    (40, 12, 3000, 0, 32, False),     # paged
+    (600, 13, 1500, 0, 0, False),     # more sequences than the plan keeps in registers, more than 256 pieces
+    (7, 14, 9000, 0, 0, False),       # few sequences: many pieces each
+    (9, 15, 5000, 320, 0, False),     # a requested piece length
+    (70, 16, 9000, 256, 0, True),     # first 64 at most 16 pieces each (per-sequence writes), the rest 17-36 (whole-wave)
 ])
-def test_device_plan_matches_its_definition(B, seed, max_len, split, bs):
+def test_device_plan_matches_its_definition(B, seed, max_len, split, bs, mixed):
     """The plan the device leaves in the workspace (laid out as kvattn.h documents it).
 
     With split_tokens 0 the piece length t is the shortest multiple of 32, at least 256, that cuts the
@@ -217,6 +218,9 @@ def test_device_plan_matches_its_definition(B, seed, max_len, split, bs):
 
     rng = np.random.default_rng(seed)
     lens = rng.integers(0, max_len + 1, size=B).astype(np.int32)
+    if mixed:
+        lens[:64] = rng.integers(0, 16 * 256 + 1, size=64)
+        lens[64:] = rng.integers(16 * 256 + 1, max_len + 1, size=B - 64)
     lens[0], lens[-1] = 0, 1
     h = 16
     w = W.MlaWorkload(f"mla_plan_def_{B}", B, h, max_len, 950 + seed, 1 / np.sqrt(192), block_size=bs)
