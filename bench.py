@@ -259,6 +259,9 @@ SWEEP = [
     "llama3_70b_gqa_fp8_h64_g8_b64_s8192",
     "mistral7b_swa_h32_g8_b16_s32768_w4096",
     "deepseek_v2_mla_paged_h128_b32_bs64_len1_16384",
+    "llama3_70b_gqa_h64_g8_b1_s131072",
+    "llama3_70b_mqa_h64_g1_b1_s131072",
+    "deepseek_v2_mla_h128_b1_s131072",
 ]
 
 

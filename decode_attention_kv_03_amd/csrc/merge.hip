@@ -7,7 +7,7 @@
 //     M = max_s lse_s,  w_s = 2^(lse_s - M),  o = sum_s w_s o_s / sum_s w_s,
 //     lse = M + log2(sum_s w_s)
 // (softmax over a union of token sets).  One workgroup per (sequence, head),
-// of one wave, or of up to eight when a row has many splits (a long
+// of one wave, or of up to sixteen when a row has many splits (a long
 // sequence): every wave then finds M and the normaliser over all splits
 // itself (a few loads per lane), sums the weighted partials of its share of
 // the splits, and the waves' sums are added through LDS.
@@ -28,7 +28,7 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <int DV, bool BF16>
-__global__ __launch_bounds__(512) void lse_merge(DecodeArgs a) {
+__global__ __launch_bounds__(1024) void lse_merge(DecodeArgs a) {
   // Lane l handles float4 columns c = l % kRowLanes (+ kRowLanes * k) of
   // the splits s = l / kRowLanes + kSplitGroups * u.  Every load of a round
   // (the splits' log-sum-exps and partial outputs) is issued before any is
@@ -73,15 +73,22 @@ __global__ __launch_bounds__(512) void lse_merge(DecodeArgs a) {
   constexpr int kRound = kSplitGroups * kU;  // splits per round of one wave; wave w takes rounds w, w + n_waves, ...
   if (nv > wave * kRound) load_round(wave * kRound);  // in flight while the maximum and the normaliser are found
 
-  // Lane l keeps the log-sum-exp of split l; splits past 64 are reread.
-  const float lv = lane < nv ? pl[lane] : -INFINITY;
-  float M = lv;
-  for (int s = lane + 64; s < nv; s += 64) M = fmaxf(M, pl[s]);
+  // Lane l keeps the log-sum-exps of splits l, l + 64, ..., l + 448, all
+  // loaded before any is used; splits past 512 are reread.
+  constexpr int kLse = 8;
+  float lv[kLse];
+#pragma unroll
+  for (int i = 0; i < kLse; ++i) lv[i] = lane + 64 * i < nv ? pl[lane + 64 * i] : -INFINITY;
+  float M = lv[0];
+#pragma unroll
+  for (int i = 1; i < kLse; ++i) M = fmaxf(M, lv[i]);
+  for (int s = lane + 64 * kLse; s < nv; s += 64) M = fmaxf(M, pl[s]);
   M = wave_reduce_max(M);
   float L = 0.f;
   if (M != -INFINITY) {
-    L = lane < nv ? fast_exp2(lv - M) : 0.f;
-    for (int s = lane + 64; s < nv; s += 64) L += fast_exp2(pl[s] - M);
+#pragma unroll
+    for (int i = 0; i < kLse; ++i) L += fast_exp2(lv[i] - M);  // 2^-inf = 0 past the end
+    for (int s = lane + 64 * kLse; s < nv; s += 64) L += fast_exp2(pl[s] - M);
   }
   L = wave_reduce_sum(L);
   const bool empty = !(L > 0.f);
@@ -109,17 +116,19 @@ __global__ __launch_bounds__(512) void lse_merge(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[k][e] += __shfl_xor(acc[k][e], m, 64);
   if (n_waves > 1) {
-    // The other waves' sums, added by wave 0.
-    __shared__ f32x4 red[7][kRowLanes * kCols];
+    // The other waves' sums, added by wave 0 (the launch sizes the LDS:
+    // kRowLanes * kCols float4 per wave past the first, none for one wave).
+    extern __shared__ f32x4 red[];
+    constexpr int kRow = kRowLanes * kCols;
     if (wave > 0 && sg == 0) {
 #pragma unroll
-      for (int k = 0; k < kCols; ++k) red[wave - 1][c + kRowLanes * k] = acc[k];
+      for (int k = 0; k < kCols; ++k) red[(wave - 1) * kRow + c + kRowLanes * k] = acc[k];
     }
     __syncthreads();
     if (wave > 0) return;
     for (int w2 = 1; w2 < n_waves; ++w2)
 #pragma unroll
-      for (int k = 0; k < kCols; ++k) acc[k] += red[w2 - 1][c + kRowLanes * k];
+      for (int k = 0; k < kCols; ++k) acc[k] += red[(w2 - 1) * kRow + c + kRowLanes * k];
   }
   if (sg == 0) {
 #pragma unroll
@@ -141,10 +150,12 @@ __global__ __launch_bounds__(512) void lse_merge(DecodeArgs a) {
 
 hipError_t launch_merge(const DecodeArgs& a, bool out_bf16, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.batch);
-  // One wave per row, or one per 32 splits (two rounds of loads each) up to eight.
-  const dim3 block(64 * std::min(8, std::max(1, (a.n_split + 31) / 32)));
-  if (out_bf16) lse_merge<kHeadDim, true><<<grid, block, 0, stream>>>(a);
-  else lse_merge<kHeadDim, false><<<grid, block, 0, stream>>>(a);
+  // One wave per row, or one per 32 splits (two rounds of loads each) up to sixteen.
+  const int waves = std::min(16, std::max(1, (a.n_split + 31) / 32));
+  // LDS for the waves' sums: one row of kHeadDim floats per wave past the first.
+  const size_t lds = (size_t)(waves - 1) * kHeadDim * sizeof(float);
+  if (out_bf16) lse_merge<kHeadDim, true><<<grid, 64 * waves, lds, stream>>>(a);
+  else lse_merge<kHeadDim, false><<<grid, 64 * waves, lds, stream>>>(a);
   return hipGetLastError();
 }
 

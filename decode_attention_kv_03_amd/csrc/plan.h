@@ -32,15 +32,21 @@ inline int32_t plan_gqa_split(int32_t batch, int32_t h, int32_t g, int32_t max_s
   if (requested > 0) return (int32_t)std::min<int64_t>(requested, round_up(S, KVATTN_SPLIT_ALIGN));
   const int64_t units = (int64_t)batch * g;
   const int64_t r = h / g;
+  // A split writes r partial rows: at least 16 r tokens keep them small next
+  // to the split's own reads, unless that leaves the chip short of
+  // workgroups (few sequences and KV heads with many query heads each, e.g.
+  // one long MQA sequence); then the floor is 256 tokens.
   const int64_t min_chunk = std::max<int64_t>(256, 16 * r);
-  int64_t chunk;
+  int64_t even;
   if (paged) {
-    chunk = round_up((S * units + 4 * kCUs - 1) / (4 * kCUs), KVATTN_SPLIT_ALIGN);
-    chunk = std::min<int64_t>(std::max(chunk, min_chunk), 2048);
+    even = round_up((S * units + 4 * kCUs - 1) / (4 * kCUs), KVATTN_SPLIT_ALIGN);
   } else {
     const int64_t want_splits = std::max<int64_t>(1, (2 * kCUs + units - 1) / units);
-    chunk = std::max(round_up((S + want_splits - 1) / want_splits, KVATTN_SPLIT_ALIGN), min_chunk);
+    even = round_up((S + want_splits - 1) / want_splits, KVATTN_SPLIT_ALIGN);
   }
+  int64_t chunk = std::max(even, min_chunk);
+  if (units * ((S + chunk - 1) / chunk) < 2 * kCUs) chunk = std::max<int64_t>(even, 256);
+  if (paged) chunk = std::min<int64_t>(chunk, 2048);
   return (int32_t)std::min(chunk, round_up(S, KVATTN_SPLIT_ALIGN));
 }
 

@@ -87,6 +87,11 @@ WORKLOADS = {
         # Paged latent cache: 64-token blocks, lengths uniform on [1, 16384], a random block permutation.
         MlaWorkload("deepseek_v2_mla_paged_h128_b32_bs64_len1_16384", 32, 128, 16384, 7, 1 / math.sqrt(192),
                     block_size=64),
+        # One sequence of 128K tokens: the long-context decode of a single request, where the split
+        # over tokens alone fills the chip ("MQA, GQA, and MLA" section 9 speaks of MLA at 128k context).
+        GqaWorkload("llama3_70b_gqa_h64_g8_b1_s131072", 1, 64, 8, 128, 131072, "bf16", 35, 1 / math.sqrt(128)),
+        GqaWorkload("llama3_70b_mqa_h64_g1_b1_s131072", 1, 64, 1, 128, 131072, "bf16", 36, 1 / math.sqrt(128)),
+        MlaWorkload("deepseek_v2_mla_h128_b1_s131072", 1, 128, 131072, 9, 1 / math.sqrt(192)),
         # The same DeepSeek-V2 layer in the naive form: per-head query and synthetic up-projection weights.
         MlaWorkload("deepseek_v2_mla_explicit_h128_b32_s8192", 32, 128, 8192, 8, 1 / math.sqrt(192), form="explicit"),
     ]

@@ -9,8 +9,10 @@ from decode_attention_kv_03_amd import workloads as W
 def test_named_workloads_have_expected_shapes():
     c = W.WORKLOADS
     assert c["gqa_h8_g2_d128_s512_b1_f32"].dtype == "f32"
-    w70 = [c[n] for n in c if n.startswith("llama3_70b") and c[n].dtype == "bf16"]
+    w70 = [c[n] for n in c if n.startswith("llama3_70b") and c[n].dtype == "bf16" and c[n].seq_len == 8192]
     assert sorted((w.num_kv_heads, w.batch) for w in w70) == [(1, 64), (8, 64), (64, 8)]
+    long = [c[n] for n in c if c[n].seq_len == 131072]
+    assert sorted((getattr(w, "num_kv_heads", 0), w.batch) for w in long) == [(0, 1), (1, 1), (8, 1)]
     f8 = c["llama3_70b_gqa_fp8_h64_g8_b64_s8192"]
     assert (f8.dtype, f8.num_q_heads, f8.num_kv_heads, f8.batch, f8.seq_len) == ("fp8", 64, 8, 64, 8192)
     m = c["deepseek_v2_mla_h128_b32_s8192"]
