@@ -133,6 +133,13 @@ def test_split_planner():
     assert f(64, 64, 8, 8192, 0, 0) == 8192       # 512 units, no split
     assert f(8, 64, 64, 8192, 0, 0) == 8192
     assert f(128, 64, 8, 32768, 16, 0) == 2048    # paged
+    # at least 16 r tokens per split (r = h / g partial rows), unless that leaves fewer than two
+    # workgroups per CU: then at least 256
+    assert f(4, 64, 1, 8192, 0, 0) == 256         # 16 r = 1024 would give 32 workgroups
+    assert f(1, 64, 1, 131072, 0, 0) == 256       # one long MQA sequence: 512 splits
+    assert f(1, 64, 1, 131072, 16, 0) == 256      # paged
+    assert f(1, 32, 1, 131072, 0, 0) == 256       # 16 r = 512 would give 256
+    assert f(2, 64, 1, 1 << 20, 0, 0) == 4096     # long enough: 256 splits each, above the floor
     m = lib.kvattn_mla_split_tokens
     assert m(32, 128, 8192, 0, 0) == 1024     # 32 x 8192 tokens over 256 compute units
     assert m(32, 128, 16384, 64, 0) == 2048

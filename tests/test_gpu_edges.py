@@ -134,7 +134,7 @@ LONG = 65536
 
 
 @pytest.mark.parametrize("h,g,split,dtype", [(32, 8, 64, "bf16"), (8, 2, 0, "bf16"), (16, 2, 128, "fp8"),
-                                             (8, 1, 0, "f32")])
+                                             (8, 1, 0, "f32"), (64, 1, 0, "bf16")])
 def test_long_single_sequence_gqa(h, g, split, dtype):
     w = W.GqaWorkload(f"long_{dtype}", 1, h, g, 128, LONG, dtype, 70 + h, 1 / np.sqrt(128))
     from decode_attention_kv_03_amd import kvattn
