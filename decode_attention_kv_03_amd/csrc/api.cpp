@@ -211,6 +211,7 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   const int32_t full_split = plan_gqa_split(batch, num_q_heads, num_kv_heads, max_seq_len, paged, split_tokens);
   const int32_t full_n = n_splits(max_seq_len, full_split);
   int32_t split = full_split, nsplit = full_n;
+  bool absorb = false;  // the last split of a sequence may hold more than `split` tokens
   if (window > 0) {
     const int32_t span = (int32_t)std::min<int64_t>(max_seq_len, (int64_t)window + 63);
     split = plan_gqa_split(batch, num_q_heads, num_kv_heads, span, paged, split_tokens);
@@ -218,6 +219,24 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
     if (nsplit > full_n) {
       split = (int32_t)round_up((span + full_n - 1) / full_n, KVATTN_SPLIT_ALIGN);
       nsplit = n_splits(span, split);
+    }
+    // The automatic plan may instead size the splits for the window itself,
+    // the last split of a sequence also taking the up to 63 tokens of the
+    // aligned start (every kernel ends a sequence's last split at its
+    // length): an aligned 4096-token window in four splits then reads 16
+    // tiles per split instead of 17.  Taken when that shortens the splits
+    // without adding any, on grids of one workgroup per split (the
+    // persistent form's work list cuts every split at `split` tokens).
+    if (split_tokens == 0) {
+      const int32_t wlen = std::min(max_seq_len, window);
+      const int32_t s2 = plan_gqa_split(batch, num_q_heads, num_kv_heads, wlen, paged, 0);
+      const int32_t n2 = n_splits(wlen, s2);
+      if (s2 < split && n2 <= nsplit && (int64_t)n2 * s2 < span &&
+          gqa_persistent_layout(cache.kind, batch, num_kv_heads, n2, paged ? block_size : 0, 0).total == 0) {
+        split = s2;
+        nsplit = n2;
+        absorb = true;
+      }
     }
   }
   // Partial outputs are fp32 for an fp32 cache and bf16 otherwise (the
@@ -229,7 +248,10 @@ kvattn_status gqa_run(const kvattn::LaunchEvents& ev, const void* q, const GqaCa
   // it (the bf16 partials leave room for it in the size the query reports).
   const GqaPersistentLayout pl =
       gqa_persistent_layout(cache.kind, batch, num_kv_heads, nsplit, paged ? block_size : 0, need);
-  const bool persistent = pl.total > 0 && pl.total <= wsrc.bytes && (wsrc.resolve != nullptr || wsrc.ptr != nullptr);
+  // (Its work list cuts every split at `split` tokens, so a plan whose last
+  // split takes more keeps one workgroup per split.)
+  const bool persistent =
+      !absorb && pl.total > 0 && pl.total <= wsrc.bytes && (wsrc.resolve != nullptr || wsrc.ptr != nullptr);
   if (persistent) need = pl.total;
   void* workspace = wsrc.ptr;
   if (need > 0) {

@@ -36,7 +36,8 @@ __global__ __launch_bounds__(256) void gqa_split_f32(DecodeArgs a) {
   const int t_begin = window_base(len, a.window) + split * a.split_tokens;
   const bool final_out = (a.n_split == 1);
   if (!final_out && t_begin >= len) return;
-  const int t_end = min(len, t_begin + a.split_tokens);
+  // The last split ends at the sequence's end (it also takes a window's aligned start).
+  const int t_end = split == a.n_split - 1 ? len : min(len, t_begin + a.split_tokens);
 
   __shared__ __attribute__((aligned(16))) float kt[kTileF * kRowF];
   __shared__ __attribute__((aligned(16))) float vt[kTileF * kRowF];

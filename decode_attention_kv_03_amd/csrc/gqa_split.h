@@ -93,7 +93,10 @@ __device__ __forceinline__ bool gqa_work(const DecodeArgs& a, GqaWork& w) {
   w.t_begin = window_base(len, a.window) + w.split * a.split_tokens;
   w.final_out = (a.n_split == 1);
   if (!w.final_out && w.t_begin >= len) return false;  // the merge only reads splits that hold tokens
-  w.t_end = min(len, w.t_begin + a.split_tokens);
+  // The last split ends at the sequence's end: a window's splits are sized
+  // for the window, and the last one also takes the tokens of its aligned
+  // start (otherwise n_split splits reach past the end anyway).
+  w.t_end = w.split == a.n_split - 1 ? len : min(len, w.t_begin + a.split_tokens);
   const int ntok = w.t_end - w.t_begin;
   w.n_tiles = ntok > 0 ? (ntok + kTile - 1) / kTile : 0;
   return true;

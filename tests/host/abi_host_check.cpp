@@ -86,8 +86,11 @@ static void window_sweep() {
               const kvattn::DecodeArgs& a = stub::last.args;
               const int64_t span = W < S ? (int64_t)W + 63 < S ? W + 63 : S : S;
               CHECK(a.split_tokens > 0 && a.split_tokens % 64 == 0, "split %d", a.split_tokens);
-              CHECK((int64_t)a.n_split * a.split_tokens >= span, "S=%d W=%d: %d x %d < %lld", S, W, a.n_split,
-                    a.split_tokens, (long long)span);
+              // The last split runs to the sequence's end, taking up to 63 tokens of a window's aligned start.
+              CHECK((int64_t)a.n_split * a.split_tokens + 63 >= span, "S=%d W=%d: %d x %d + 63 < %lld", S, W,
+                    a.n_split, a.split_tokens, (long long)span);
+              CHECK((int64_t)a.n_split * a.split_tokens >= span || W == 0 || stub::last.gqa_plans == 0,
+                    "a persistent call whose last split would run past n_split x split");
               CHECK(a.n_split == 1 || (int64_t)(a.n_split - 1) * a.split_tokens < span, "empty split");
               const size_t need = a.n_split > 1 ? (size_t)B * hg[0] * a.n_split * 129 * 4 : 0;
               CHECK(need <= ws, "need %zu > queried %zu", need, ws);

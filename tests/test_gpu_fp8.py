@@ -109,6 +109,26 @@ def test_fp8_sliding_window(B, h, g, lens, window, split):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
 
 
+@pytest.mark.parametrize("block_size", [0, 16])
+def test_fp8_sliding_window_last_split_takes_the_aligned_start(block_size):
+    """The automatic plan sizes its splits for the window (128 units); the last split of each
+    sequence also takes the up to 63 tokens its 64-aligned start adds."""
+    # a paged cache plans on ragged-length grounds: there a 4096-token window takes this plan
+    B, h, g = 16, 32, 8
+    S, window = (4400, 4096) if block_size else (2400, 2048)
+    rng = np.random.default_rng(4096 + block_size)
+    lens = rng.integers(window + 64, S + 1, size=B)
+    lens[lens % 64 == 0] -= 1
+    w = W.GqaWorkload(f"fp8win_last_{block_size}", B, h, g, 128, S, "fp8", 4200 + block_size, 1 / np.sqrt(128),
+                      block_size=block_size)
+    note(f"fp8 window={window} B={B} lens={lens.tolist()} block_size={block_size} auto split")
+    x = W.make_gqa_inputs(w, DEV, lens=lens, poison_tail=True)
+    ref, ref_lse = reference(x, window=window)
+    out, lse = run(x, split_tokens=0, window=window)
+    assert_close(out.float().cpu().numpy(), ref, "window, last split past n_split x split")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
+
+
 @pytest.mark.parametrize("B,h,g,max_len,block_size,window", [
     (5, 64, 8, 900, 16, 0),     # power-of-two blocks of >= 8 tokens: scalar table loads per 8 rows
     (4, 16, 4, 600, 8, 0),

@@ -271,6 +271,28 @@ def test_sliding_window_contiguous(B, h, g, lens, window, split, dtype):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=tol, rtol=1e-4)
 
 
+@pytest.mark.parametrize("dtype,block_size", [("bf16", 0), ("bf16", 16), ("f32", 0)])
+def test_sliding_window_last_split_takes_the_aligned_start(dtype, block_size):
+    """128 (sequence, KV head) units and a window (2048 tokens, 4096 paged): the automatic plan sizes its splits for
+    the window (four of 512 tokens contiguous, eight of 512 paged) and the last split of each sequence also takes the up to 63 tokens its
+    64-aligned start adds (lengths not multiples of 64)."""
+    # a paged cache plans on ragged-length grounds: there a 4096-token window takes this plan
+    B, h, g = 16, 32, 8
+    S, window = (4400, 4096) if block_size else (2400, 2048)
+    rng = np.random.default_rng(2048 + block_size)
+    lens = rng.integers(window + 64, S + 1, size=B)
+    lens[lens % 64 == 0] -= 1
+    w = W.GqaWorkload(f"win_last_{dtype}_{block_size}", B, h, g, 128, S, dtype, 2100 + block_size,
+                      1 / np.sqrt(128), block_size=block_size)
+    note(f"window={window} B={B} lens={lens.tolist()} {dtype} block_size={block_size} auto split")
+    x = W.make_gqa_inputs(w, DEV, lens=lens, poison_tail=True)
+    ref, ref_lse = reference(x, window=window)
+    out, lse = run(x, split_tokens=0, window=window)
+    assert_close(out.float().cpu().numpy(), ref, dtype, "window, last split past n_split x split")
+    tol = LSE_ATOL_F32 if dtype == "f32" else LSE_ATOL
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=tol, rtol=1e-4)
+
+
 @pytest.mark.parametrize("block_size,window", [(16, 200), (16, 1000), (5, 77)])
 def test_sliding_window_paged(block_size, window):
     pw = W.shrink(W.WORKLOADS["paged_gqa_h64_g8_b128_bs16_len1_32768"], batch=5, seq_len=900)
