@@ -83,3 +83,43 @@ def test_random_mla_shape(i):
     np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
     del x
     torch.cuda.empty_cache()
+
+
+def persistent_case(i):
+    rng = np.random.default_rng(9000 + i)
+    dtype = ["bf16", "fp8"][i % 2]
+    g = int(rng.choice([4, 8]))
+    h = g * int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(32, 65))
+    S = int(rng.integers(1100, 2001))  # with B >= 32, g >= 4 and 64-token splits: more than 2048 splits
+    lens = rng.integers(0, S + 1, size=B)
+    # power-of-two blocks of at least one copy instruction's rows (4 bf16, 8 fp8), where full tiles need
+    # no LDS table
+    block_size = int(rng.choice([4, 8, 16, 32] if dtype == "bf16" else [8, 16, 32]))
+    split = int(rng.choice([64, 128]))
+    if B * g * -(-S // split) <= 2048:
+        split = 64
+    return dtype, h, g, B, S, lens.astype(np.int64), block_size, split
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_persistent_shape(i):
+    """Paged batches cut into more than 2048 splits: the persistent form with its device work list."""
+    dtype, h, g, B, S, lens, block_size, split = persistent_case(i)
+    slots = B * g * -(-S // split)
+    assert slots > 2048, "the grid must be large enough for the persistent form"
+    G.note(f"random persistent {i}: {dtype} h={h} g={g} B={B} S={S} block_size={block_size} split={split} "
+           f"({slots} splits)")
+    w = W.GqaWorkload(f"rand_pers_{i}", B, h, g, 128, S, dtype, 9000 + i, 1 / np.sqrt(128), block_size=block_size)
+    x = W.make_gqa_inputs(w, DEV, lens=lens, poison_tail=True)
+    if dtype == "fp8":
+        ref, ref_lse = F8.reference(x)
+        out, lse = F8.run(x, split_tokens=split)
+        F8.assert_close(out.float().cpu().numpy(), ref, f"random persistent {i}")
+    else:
+        ref, ref_lse = G.reference(x)
+        out, lse = G.run(x, split_tokens=split)
+        G.assert_close(out.float().cpu().numpy(), ref, dtype, f"random persistent {i}")
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=LSE_ATOL, rtol=1e-4)
+    del x
+    torch.cuda.empty_cache()
