@@ -151,6 +151,9 @@ kvattn_status kvattn_gqa_decode(const void* q, const void* k_cache, const void* 
  * Arguments and layouts are those of kvattn_gqa_decode (token indices and
  * block-table lookups stay absolute); the workspace kvattn_gqa_workspace_bytes
  * reports for the same arguments is enough.  window < 0 is KVATTN_ERR_INVALID.
+ * A window's tokens are read from the multiple of 64 at or below its first;
+ * with split_tokens = 0 the library may size the splits for the window
+ * itself, the last split of a sequence then holding up to 63 tokens more.
  */
 kvattn_status kvattn_gqa_decode_window(const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* block_table, const int32_t* seq_lens, void* out,
